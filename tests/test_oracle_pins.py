@@ -1,0 +1,92 @@
+"""The CPU oracle against its pins (see ``tests/pins.py`` for what each pins)."""
+import numpy as np
+import pytest
+
+import exact_model as em
+import pins
+
+DTYPES = ["bf16", "fp16", "fp32"]
+
+
+def test_hand_cases_agree_with_exact_model():
+    # the hand derivations and the exact model are two independent routes
+    for dtype, ins, want in pins.load_hand_cases():
+        got = em.allreduce_column(ins, dtype)
+        if em.is_nan_bits(want, dtype):
+            assert em.is_nan_bits(got, dtype)
+        else:
+            assert got == want, (dtype, [hex(v) for v in ins])
+
+
+def test_hand_cases(orc):
+    pins.pin_hand_cases(orc)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bruteforce_exhaustive_R3(orc, dtype):
+    pins.pin_bruteforce_exhaustive(orc, dtype, R=3)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bruteforce_exhaustive_R2(orc, dtype):
+    pins.pin_bruteforce_exhaustive(orc, dtype, R=2)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("R,ncols", [(8, 3000), (16, 1500), (32, 800)])
+def test_bruteforce_random(orc, dtype, R, ncols):
+    pins.pin_bruteforce_random(orc, dtype, R, ncols)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("R", [2, 3, 8, 16, 32])
+def test_integer_closed_form(orc, dtype, R):
+    pins.pin_integer_closed_form(orc, dtype, R)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_exact_partial_sums_give_correctly_rounded_sum(orc, dtype):
+    pins.pin_exact_partials(orc, dtype)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_invariants(orc, dtype):
+    pins.pin_invariants(orc, dtype)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("R", [2, 8, 32])
+def test_error_bound(orc, dtype, R):
+    pins.pin_error_bound(orc, dtype, R)
+
+
+def test_converters_sample(orc):
+    pins.pin_converters(orc, pins.converter_patterns_sample())
+
+
+def test_widen_fp16_exhaustive(orc):
+    pins.pin_widen_fp16(orc)
+
+
+def test_converters_exhaustive(orc):
+    """All 2^32 binary32 patterns, in slices, against torch and numpy."""
+    step = 1 << 27
+    for start in range(0, 1 << 32, step):
+        pins.pin_converters_slice(orc, start, step)
+
+
+def test_thread_count_does_not_change_bits(orc):
+    rng = np.random.default_rng(3)
+    x = pins.random_bits(rng, "bf16", (8, 100_003), emin=-20, emax=20)
+    a = orc.allreduce(x, "bf16", nthreads=1)
+    b = orc.allreduce(x, "bf16", nthreads=7)
+    assert np.array_equal(a, b)
+
+
+def test_in_place_equals_out_of_place(orc):
+    rng = np.random.default_rng(4)
+    x = pins.random_bits(rng, "bf16", (8, 5000), emin=-20, emax=20)
+    want = orc.allreduce(x, "bf16")
+    y = x.copy()
+    orc.allreduce_into(list(y), list(y), "bf16")
+    assert np.array_equal(y, want)
