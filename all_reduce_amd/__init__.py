@@ -1,0 +1,264 @@
+"""Python binding of the MI355X sum all-reduce over R simulated ranks.
+
+The functions named ``ar*`` are the C ABI of ``include/ar_allreduce.h``, one
+for one, over ctypes: arguments are marshalled and the result code is
+returned, nothing else happens here.  :class:`Comm` and :func:`rank_buffers`
+are conveniences on top for torch tensors; torch supplies device memory and
+streams only.  Every step of the all-reduce runs in the HIP kernels of
+``libar_allreduce.so``; there is no other implementation to fall back to, so a
+missing library raises instead of running anything.
+"""
+from __future__ import annotations
+
+import ctypes
+from enum import IntEnum
+from pathlib import Path
+from typing import Sequence
+
+LIBRARY = Path(__file__).resolve().parent / "_lib" / "libar_allreduce.so"
+HEADER = Path(__file__).resolve().parent.parent / "include" / "ar_allreduce.h"
+
+
+class arResult(IntEnum):
+    arSuccess = 0
+    arInvalidArgument = 1
+    arUnsupported = 2
+    arInvalidUsage = 3
+    arHipError = 4
+    arTimeout = 5
+    arInternalError = 6
+
+
+class arDataType(IntEnum):
+    arBfloat16 = 0
+    arFloat16 = 1
+    arFloat32 = 2
+
+
+class arRedOp(IntEnum):
+    arSum = 0
+
+
+class arProtocol(IntEnum):
+    arProtoLL = 0
+    arProtoHB = 1
+
+
+class arOption(IntEnum):
+    arOptPollTimeoutUs = 0
+    arOptLLBlocksPerRank = 1
+    arOptHBBlocksPerCU = 2
+    arOptHBNonTemporal = 3
+    arOptDebugFlagSkew = 4
+    arOptHBUnroll = 5
+    arOptLLThreads = 6
+
+
+AR_MAX_RANKS = 32
+
+
+class ArError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = arResult(code)
+        super().__init__(f"{where}: {arGetErrorString(code)}")
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIBRARY.exists():
+        raise RuntimeError(f"{LIBRARY} is missing: build it with `python -m all_reduce_amd.build`")
+    lib = ctypes.CDLL(str(LIBRARY))
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "arCommCreate": ([ctypes.POINTER(vp), i32, i32, sz], i32),
+        "arCommDestroy": ([vp], i32),
+        "arCommReset": ([vp, vp], i32),
+        "arCommGetAsyncError": ([vp, ctypes.POINTER(i32)], i32),
+        "arCommSetOption": ([vp, i32, i64], i32),
+        "arCommGetOption": ([vp, i32, ctypes.POINTER(i64)], i32),
+        "arAllReduce": ([ctypes.POINTER(vp), ctypes.POINTER(vp), sz, i32, i32, i32, i32, vp, vp], i32),
+        "arGetErrorString": ([i32], ctypes.c_char_p),
+        "arGetVersion": ([], i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+# ---- the C ABI, one Python function per entry point -----------------------
+def arGetErrorString(result: int) -> str:
+    return library().arGetErrorString(int(result)).decode()
+
+
+def arGetVersion() -> int:
+    return library().arGetVersion()
+
+
+def arCommCreate(device: int, max_ranks: int, max_ll_bytes_per_rank: int):
+    """Returns (result code, communicator handle or None)."""
+    h = ctypes.c_void_p()
+    r = library().arCommCreate(ctypes.byref(h), device, max_ranks, max_ll_bytes_per_rank)
+    return r, (h.value if r == 0 else None)
+
+
+def arCommDestroy(comm) -> int:
+    return library().arCommDestroy(comm)
+
+
+def arCommReset(comm, stream) -> int:
+    return library().arCommReset(comm, stream)
+
+
+def arCommGetAsyncError(comm):
+    """Returns (result code, recorded asynchronous error)."""
+    e = ctypes.c_int(0)
+    r = library().arCommGetAsyncError(comm, ctypes.byref(e))
+    return r, e.value
+
+
+def arCommSetOption(comm, option: int, value: int) -> int:
+    return library().arCommSetOption(comm, int(option), int(value))
+
+
+def arCommGetOption(comm, option: int):
+    v = ctypes.c_int64(0)
+    r = library().arCommGetOption(comm, int(option), ctypes.byref(v))
+    return r, v.value
+
+
+def arAllReduce(sendbufs: Sequence[int] | None, recvbufs: Sequence[int] | None, count: int,
+                dtype: int, op: int, nranks: int, protocol: int, comm, stream) -> int:
+    """Device pointers as integers; ``None`` passes a NULL array."""
+    vp = ctypes.c_void_p
+    s = None if sendbufs is None else (vp * max(1, len(sendbufs)))(*sendbufs)
+    d = None if recvbufs is None else (vp * max(1, len(recvbufs)))(*recvbufs)
+    return library().arAllReduce(s, d, count, int(dtype), int(op), nranks, int(protocol),
+                                 comm, stream)
+
+
+# ---- torch conveniences ---------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(dtype) -> arDataType:
+    torch = _torch()
+    table = {torch.bfloat16: arDataType.arBfloat16, torch.float16: arDataType.arFloat16,
+             torch.float32: arDataType.arFloat32}
+    if dtype not in table:
+        raise ArError(arResult.arUnsupported, f"dtype {dtype}")
+    return table[dtype]
+
+
+def protocol_code(protocol) -> arProtocol:
+    if isinstance(protocol, str):
+        return {"ll": arProtocol.arProtoLL, "hb": arProtocol.arProtoHB}[protocol.lower()]
+    return arProtocol(protocol)
+
+
+def rank_buffers(nranks: int, count: int, dtype, device, align: int = 256):
+    """One allocation holding ``nranks`` buffers of ``count`` elements.
+
+    Rank r's buffer starts at ``base + r * stride`` with the stride rounded up
+    to ``align`` bytes.  Returns (plane, views): ``plane`` is the
+    (nranks, stride_elems) tensor, ``views[r]`` rank r's ``count`` elements."""
+    torch = _torch()
+    es = torch.empty((), dtype=dtype).element_size()
+    stride = -(-max(count, 1) * es // align) * align // es
+    plane = torch.empty((nranks, stride), dtype=dtype, device=device)
+    return plane, [plane[r, :count] for r in range(nranks)]
+
+
+class Comm:
+    """Owns an ``arComm_t`` on one device; ``all_reduce`` over torch tensors."""
+
+    def __init__(self, device=None, max_ranks: int = AR_MAX_RANKS,
+                 max_ll_bytes_per_rank: int = 1 << 20):
+        torch = _torch()
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None \
+            else torch.device(device)
+        self.device = dev
+        r, h = arCommCreate(dev.index if dev.index is not None else 0, max_ranks,
+                            max_ll_bytes_per_rank)
+        if r != 0:
+            raise ArError(r, "arCommCreate")
+        self.handle = h
+        self.max_ranks = max_ranks
+        self.max_ll_bytes_per_rank = max_ll_bytes_per_rank
+
+    def close(self):
+        if self.handle is not None:
+            r = arCommDestroy(self.handle)
+            self.handle = None
+            if r != 0:
+                raise ArError(r, "arCommDestroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _stream(self, stream):
+        torch = _torch()
+        s = torch.cuda.current_stream(self.device) if stream is None else stream
+        return s.cuda_stream
+
+    def set_option(self, option, value: int):
+        r = arCommSetOption(self.handle, option, value)
+        if r != 0:
+            raise ArError(r, "arCommSetOption")
+
+    def get_option(self, option) -> int:
+        r, v = arCommGetOption(self.handle, option)
+        if r != 0:
+            raise ArError(r, "arCommGetOption")
+        return v
+
+    def reset(self, stream=None):
+        r = arCommReset(self.handle, self._stream(stream))
+        if r != 0:
+            raise ArError(r, "arCommReset")
+
+    def async_error(self) -> arResult:
+        r, e = arCommGetAsyncError(self.handle)
+        if r != 0:
+            raise ArError(r, "arCommGetAsyncError")
+        return arResult(e)
+
+    def all_reduce(self, send, recv=None, protocol="hb", stream=None):
+        """Sum all-reduce of the tensors in ``send`` into ``recv`` (default: in place)."""
+        if recv is None:
+            recv = send
+        if len(send) != len(recv) or not send:
+            raise ValueError("need one receive tensor per send tensor")
+        t0 = send[0]
+        for t in (*send, *recv):
+            if t.device != self.device:
+                raise ValueError(f"tensor on {t.device}, communicator on {self.device}")
+            if t.dtype != t0.dtype or t.numel() != t0.numel():
+                raise ValueError("all rank tensors need the same dtype and size")
+            if not t.is_contiguous():
+                raise ValueError("rank tensors must be contiguous")
+        r = arAllReduce([t.data_ptr() for t in send], [t.data_ptr() for t in recv],
+                        t0.numel(), dtype_code(t0.dtype), arRedOp.arSum, len(send),
+                        protocol_code(protocol), self.handle, self._stream(stream))
+        if r != 0:
+            raise ArError(r, "arAllReduce")
+        return recv

@@ -1,0 +1,110 @@
+// ar_device.hpp -- device-side building blocks shared by the LL and HB kernels.
+//
+// Element handling for the sum all-reduce of bfloat16, float16 and float32
+// buffers (the dtypes admitted by the runtime guards of the SGLang MSCCL++
+// all-reduce guide, blog.gitcode.com, section 4.3):
+//
+//  * data moves as 32-bit words (LL packet payloads) or 128-bit vectors (HB);
+//  * each element is widened to binary32 exactly, summed in rank order
+//    0..R-1 starting from rank 0's value, and narrowed once with round to
+//    nearest even.
+//
+// Narrowing uses gfx950's packed converts (v_cvt_pk_bf16_f32,
+// v_cvt_pk_f16_f32).  They round with the wave's float mode, which the kernel
+// descriptor leaves at round-to-nearest-even with binary32 denormals kept
+// (the library is built with -fno-gpu-flush-denormals-to-zero).  The GPU
+// tests check them against an independent converter over all 2^32 inputs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ar {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Per-dtype word handling.  kPerWord elements fill one 32-bit word; kId is
+// the dtype's arDataType_t value.
+struct Bf16 {
+    static constexpr int kId = 0;
+    static constexpr int kPerWord = 2;
+    static constexpr int kBytes = 2;
+    __device__ static inline void widen(uint32_t w, float *f)
+    {
+        f[0] = __builtin_bit_cast(float, w << 16);          // low element
+        f[1] = __builtin_bit_cast(float, w & 0xffff0000u);  // high element
+    }
+    __device__ static inline uint32_t narrow(const float *f)
+    {
+        f32x2 v = {f[0], f[1]};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    }
+};
+
+struct Fp16 {
+    static constexpr int kId = 1;
+    static constexpr int kPerWord = 2;
+    static constexpr int kBytes = 2;
+    __device__ static inline void widen(uint32_t w, float *f)
+    {
+        f32x2 v = __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+        f[0] = v.x;
+        f[1] = v.y;
+    }
+    __device__ static inline uint32_t narrow(const float *f)
+    {
+        f32x2 v = {f[0], f[1]};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+    }
+};
+
+struct Fp32 {
+    static constexpr int kId = 2;
+    static constexpr int kPerWord = 1;
+    static constexpr int kBytes = 4;
+    __device__ static inline void widen(uint32_t w, float *f) { f[0] = __builtin_bit_cast(float, w); }
+    __device__ static inline uint32_t narrow(const float *f) { return __builtin_bit_cast(uint32_t, f[0]); }
+};
+
+// 128-bit global loads and stores, optionally non-temporal (streamed data
+// that is touched once should not displace other lines in L2 / MALL).
+template <bool NT>
+__device__ inline u32x4 load16(const u32x4 *p)
+{
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <bool NT>
+__device__ inline void store16(u32x4 *p, u32x4 v)
+{
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
+// Packet word of the LL protocol: low 32 bits payload, high 32 bits flag.
+// Written and read as one aligned 64-bit access at agent (device) scope, so
+// payload and flag become visible together to a reader on any XCD.
+__device__ inline void put_packet(uint64_t *slot, uint32_t payload, uint32_t flag)
+{
+    __hip_atomic_store(slot, ((uint64_t)flag << 32) | payload, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline uint64_t read_packet(const uint64_t *slot)
+{
+    return __hip_atomic_load(const_cast<uint64_t *>(slot), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline uint32_t packet_flag(uint64_t pkt) { return (uint32_t)(pkt >> 32); }
+__device__ inline uint32_t packet_payload(uint64_t pkt) { return (uint32_t)pkt; }
+
+}  // namespace ar

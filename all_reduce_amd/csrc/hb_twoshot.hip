@@ -1,0 +1,222 @@
+// hb_twoshot.hip -- the high-bandwidth (HB) all-reduce: two-shot, by chunk.
+//
+// The HB protocol of the MemoryChannel table in "MSCCL++：让 GPU 通信像 CUDA
+// 一样可编程" (infinitensor.com/news/50) moves large blocks with few
+// synchronisations, for prefill-size messages; SGLang's native
+// default_allreduce_rsag_zero_copy ("SGLang 中的 MSCCL++ All-Reduce 基准测试与
+// 推理集成指南", blog.gitcode.com, section 4.4) names its shape: a
+// reduce-scatter followed by an all-gather, straight between user buffers.
+//
+// On one GPU the R ranks' buffers are all local, so both shots fuse per tile:
+//   reduce-scatter  the workgroups of simulated rank c own chunk c
+//                   (vectors [c*C, (c+1)*C), the last chunk takes the rest) and
+//                   read that chunk from all R send buffers with 128-bit loads;
+//   reduce          binary32 accumulation in registers, rank order 0..R-1;
+//   all-gather      the reduced vector goes straight from registers to all R
+//                   receive buffers with 128-bit stores.
+// No flag and no barrier is needed: a lane loads all R inputs of a position
+// before it stores any output of that position, and positions are disjoint
+// between lanes, so in-place (recv[r] == send[r]) is safe too.
+//
+// The work is HBM-streaming: 2 * R * bytes-per-rank per call, about 0.22 flop
+// per byte at R = 8 in bf16, far below the ridge point; no LDS, no MFMA.
+// Workgroup w serves chunk w % R, so consecutive workgroups -- which the
+// dispatcher spreads round-robin over the 8 XCDs -- stream different chunks.
+#include "ar_device.hpp"
+#include "ar_internal.hpp"
+
+namespace ar {
+
+constexpr int kHBThreads = 256;
+
+// Scalar path for the elements after the last whole 16-byte vector.
+template <typename T>
+__device__ inline float load_elem(const void *base, uint64_t i)
+{
+    uint32_t w = (T::kBytes == 2) ? (uint32_t)((const uint16_t *)base)[i]
+                                  : ((const uint32_t *)base)[i];
+    float f[T::kPerWord];
+    T::widen(w, f);
+    return f[0];
+}
+
+template <typename T>
+__device__ inline void store_elem(void *base, uint64_t i, float a)
+{
+    float f[T::kPerWord] = {};
+    f[0] = a;
+    uint32_t w = T::narrow(f);
+    if constexpr (T::kBytes == 2)
+        ((uint16_t *)base)[i] = (uint16_t)w;
+    else
+        ((uint32_t *)base)[i] = w;
+}
+
+// RMAX: size of the rank table.  EXACT: nranks == RMAX at compile time;
+// otherwise nranks < RMAX arrives at run time and ranks >= nranks are skipped.
+// U: 16-byte vectors per lane per rank in flight.  NT: non-temporal access.
+template <typename T, int RMAX, bool EXACT, int U, bool NT>
+__global__ __launch_bounds__(kHBThreads) void hb_twoshot(HBParams<RMAX> p)
+{
+    const uint32_t n = EXACT ? RMAX : p.nranks;
+    const uint32_t c = blockIdx.x % n;       // chunk, and the simulated rank owning it
+    const uint32_t bb = blockIdx.x / n;      // this workgroup's place among the chunk's
+    const uint64_t c0 = (uint64_t)c * p.chunk_vec;
+    const uint64_t c1 = (c == n - 1) ? p.nvec : c0 + p.chunk_vec;
+    const uint64_t tile = (uint64_t)kHBThreads * U;
+    const uint64_t stride = (uint64_t)p.blocks_per_chunk * tile;
+
+    for (uint64_t base = c0 + (uint64_t)bb * tile; base < c1; base += stride) {
+        u32x4 v[U][RMAX];
+        // reduce-scatter: every load of the tile is issued before any use
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t i = base + (uint64_t)u * kHBThreads + threadIdx.x;
+            if (i < c1) {
+#pragma unroll
+                for (int j = 0; j < RMAX; ++j)
+                    if (EXACT || j < (int)n)
+                        v[u][j] = load16<NT>((const u32x4 *)p.rk.send[j] + i);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t i = base + (uint64_t)u * kHBThreads + threadIdx.x;
+            if (i < c1) {
+                u32x4 y;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float acc[T::kPerWord];
+                    T::widen(v[u][0][q], acc);
+#pragma unroll
+                    for (int j = 1; j < RMAX; ++j) {
+                        if (EXACT || j < (int)n) {
+                            float x[T::kPerWord];
+                            T::widen(v[u][j][q], x);
+#pragma unroll
+                            for (int e = 0; e < T::kPerWord; ++e)
+                                acc[e] = acc[e] + x[e];
+                        }
+                    }
+                    y[q] = T::narrow(acc);
+                }
+                // all-gather: the reduced vector to every rank
+#pragma unroll
+                for (int r = 0; r < RMAX; ++r)
+                    if (EXACT || r < (int)n)
+                        store16<NT>((u32x4 *)p.rk.recv[r] + i, y);
+            }
+        }
+    }
+
+    if (p.tail_elems != 0 && blockIdx.x == gridDim.x - 1 && threadIdx.x < p.tail_elems) {
+        constexpr uint64_t kPerVec = 16 / T::kBytes;
+        const uint64_t i = p.nvec * kPerVec + threadIdx.x;
+        float a = load_elem<T>(p.rk.send[0], i);
+        for (uint32_t j = 1; j < n; ++j)
+            a = a + load_elem<T>(p.rk.send[j], i);
+        for (uint32_t r = 0; r < n; ++r)
+            store_elem<T>(p.rk.recv[r], i, a);
+    }
+}
+
+namespace {
+
+template <typename T, int RMAX, bool EXACT, int U, bool NT>
+hipError_t launch_one(const HBParams<RMAX> &p, uint32_t grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((hb_twoshot<T, RMAX, EXACT, U, NT>), dim3(grid), dim3(kHBThreads), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+// Largest vectors-per-lane count compiled for a rank table size (register
+// budget: U * RMAX * 4 VGPRs of loaded data per lane).
+constexpr int max_unroll(int rmax) { return rmax <= 8 ? 4 : (rmax <= 16 ? 2 : 1); }
+
+template <typename T, int RMAX, bool EXACT>
+hipError_t launch_unroll(const HBParams<RMAX> &p, uint32_t grid, int unroll, bool nt,
+                         hipStream_t stream)
+{
+    constexpr int kMax = max_unroll(RMAX);
+    int u = unroll > kMax ? kMax : unroll;
+    if (u >= 4 && kMax >= 4)
+        return nt ? launch_one<T, RMAX, EXACT, (kMax >= 4 ? 4 : 1), true>(p, grid, stream)
+                  : launch_one<T, RMAX, EXACT, (kMax >= 4 ? 4 : 1), false>(p, grid, stream);
+    if (u >= 2 && kMax >= 2)
+        return nt ? launch_one<T, RMAX, EXACT, (kMax >= 2 ? 2 : 1), true>(p, grid, stream)
+                  : launch_one<T, RMAX, EXACT, (kMax >= 2 ? 2 : 1), false>(p, grid, stream);
+    return nt ? launch_one<T, RMAX, EXACT, 1, true>(p, grid, stream)
+              : launch_one<T, RMAX, EXACT, 1, false>(p, grid, stream);
+}
+
+template <typename T, int RMAX, bool EXACT>
+hipError_t launch_table(const void *const *send, void *const *recv, size_t count, int nranks,
+                        const arComm *comm, hipStream_t stream)
+{
+    constexpr uint64_t kPerVec = 16 / T::kBytes;
+    HBParams<RMAX> p = {};
+    for (int r = 0; r < nranks; ++r) {
+        p.rk.send[r] = send[r];
+        p.rk.recv[r] = recv[r];
+    }
+    p.nvec = count / kPerVec;
+    p.tail_elems = (uint32_t)(count % kPerVec);
+    p.chunk_vec = p.nvec / (uint64_t)nranks;
+    p.nranks = (uint32_t)nranks;
+
+    const int unroll = comm->opt[arOptHBUnroll] > 0 ? (int)comm->opt[arOptHBUnroll] : 2;
+    const bool nt = comm->opt[arOptHBNonTemporal] != 0;
+    const int per_cu = comm->opt[arOptHBBlocksPerCU] > 0 ? (int)comm->opt[arOptHBBlocksPerCU] : 4;
+    const int u_eff = unroll > max_unroll(RMAX) ? max_unroll(RMAX) : unroll;
+
+    // Enough workgroups to fill the chip, but never more than the largest
+    // chunk has tiles.
+    const uint64_t tile = (uint64_t)kHBThreads * (uint64_t)u_eff;
+    const uint64_t last_chunk = p.nvec - p.chunk_vec * (uint64_t)(nranks - 1);
+    const uint64_t tiles = (last_chunk + tile - 1) / tile;
+    uint64_t want = ((uint64_t)comm->cu_count * (uint64_t)per_cu + (uint64_t)nranks - 1) /
+                    (uint64_t)nranks;
+    uint64_t bpc = tiles < want ? tiles : want;
+    if (bpc < 1)
+        bpc = 1;
+    p.blocks_per_chunk = (uint32_t)bpc;
+    const uint32_t grid = (uint32_t)(bpc * (uint64_t)nranks);
+    return launch_unroll<T, RMAX, EXACT>(p, grid, unroll, nt, stream);
+}
+
+template <typename T>
+hipError_t launch_dtype(const void *const *send, void *const *recv, size_t count, int nranks,
+                        const arComm *comm, hipStream_t stream)
+{
+    switch (nranks) {
+    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, comm, stream);
+    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, comm, stream);
+    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, comm, stream);
+    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, comm, stream);
+    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, comm, stream);
+    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, comm, stream);
+    default: break;
+    }
+    if (nranks < 4)
+        return launch_table<T, 4, false>(send, recv, count, nranks, comm, stream);
+    if (nranks < 8)
+        return launch_table<T, 8, false>(send, recv, count, nranks, comm, stream);
+    if (nranks < 16)
+        return launch_table<T, 16, false>(send, recv, count, nranks, comm, stream);
+    return launch_table<T, 32, false>(send, recv, count, nranks, comm, stream);
+}
+
+}  // namespace
+
+hipError_t launch_hb(const void *const *send, void *const *recv, size_t count, int dtype,
+                     int nranks, const arComm *comm, hipStream_t stream)
+{
+    switch (dtype) {
+    case kBf16: return launch_dtype<Bf16>(send, recv, count, nranks, comm, stream);
+    case kFp16: return launch_dtype<Fp16>(send, recv, count, nranks, comm, stream);
+    default: return launch_dtype<Fp32>(send, recv, count, nranks, comm, stream);
+    }
+}
+
+}  // namespace ar

@@ -1,0 +1,166 @@
+/*
+ * ar_allreduce.h -- C ABI of the MI355X sum all-reduce over R rank buffers.
+ *
+ * One process, one GPU.  R "ranks" are R buffers in the GPU's HBM that stand
+ * in for the peer memory a memory-mapped channel would expose (the
+ * MemoryChannel of "MSCCL++：让 GPU 通信像 CUDA 一样可编程",
+ * infinitensor.com/news/50, section "MemoryChannel": GPU threads load and store
+ * the other GPU's memory directly).  One call reduces the R send buffers
+ * element by element and writes the sum to all R receive buffers.
+ *
+ * The call is shaped like the NCCL-compatible collective that the same page
+ * describes under "第一层：Collective API" (mscclppAllReduce as a drop-in for
+ * ncclAllReduce), with the R rank pointers of the simulated group passed as
+ * arrays.  Two protocols from the page's MemoryChannel table are offered:
+ *
+ *   arProtoLL  low latency: one kernel, flag-carrying 8-byte packets, polled
+ *              per wavefront; meant for decode-size messages.
+ *   arProtoHB  high bandwidth: two-shot reduce-scatter by chunk then
+ *              all-gather, 128-bit bulk loads and stores, no flags; meant for
+ *              prefill-size messages.
+ *
+ * Both give the same result: for every element i,
+ *     a = x_0[i];  a = a + x_j[i] for j = 1..R-1 (binary32, in this order);
+ *     recv_r[i] = a rounded to the element type (round to nearest even),
+ * which is one reading of a SUM all-reduce over float/float16/bfloat16, the
+ * operations and types admitted by the runtime guards of "SGLang 中的 MSCCL++
+ * All-Reduce 基准测试与推理集成指南" (blog.gitcode.com), section 4.3.
+ *
+ * Errors are return codes; nothing here aborts, throws or prints (except with
+ * the environment variable AR_DEBUG=1, which logs rejected calls to stderr).
+ * A result of arUnsupported means "use another all-reduce", the fallback the
+ * SGLang guide describes when a guard fails (sections 4.3 and 5).
+ *
+ * All entry points are host functions.  A communicator is used from one host
+ * thread and one stream at a time, like an NCCL communicator.
+ */
+#ifndef AR_ALLREDUCE_H
+#define AR_ALLREDUCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AR_VERSION 10000 /* 1.0.0 */
+#define AR_MAX_RANKS 32
+
+typedef struct arComm *arComm_t;
+
+/* A hipStream_t, passed as an untyped pointer so that this header does not
+ * need the HIP headers.  NULL is the device's null stream. */
+typedef void *arStream_t;
+
+typedef enum {
+    arSuccess = 0,
+    arInvalidArgument = 1, /* a pointer, size, alignment or overlap rule broken */
+    arUnsupported = 2,     /* valid request this library does not serve: fall back */
+    arInvalidUsage = 3,    /* request exceeds what the communicator was made for */
+    arHipError = 4,        /* a HIP runtime call failed */
+    arTimeout = 5,         /* an LL packet wait ran out of time (asynchronous) */
+    arInternalError = 6
+} arResult_t;
+
+typedef enum { arBfloat16 = 0, arFloat16 = 1, arFloat32 = 2 } arDataType_t;
+
+typedef enum { arSum = 0 } arRedOp_t;
+
+typedef enum { arProtoLL = 0, arProtoHB = 1 } arProtocol_t;
+
+/* Tunables and test hooks, see arCommSetOption. */
+typedef enum {
+    /* LL: longest wait for one packet, in microseconds (default 2,000,000).
+     * A wait that runs out records arTimeout in the communicator and the
+     * kernel finishes without the missing data. */
+    arOptPollTimeoutUs = 0,
+    /* LL: workgroups per simulated rank; 0 = pick from the message size. */
+    arOptLLBlocksPerRank = 1,
+    /* HB: workgroups per compute unit for the grid; 0 = default. */
+    arOptHBBlocksPerCU = 2,
+    /* HB: 1 = non-temporal loads and stores (default), 0 = ordinary ones. */
+    arOptHBNonTemporal = 3,
+    /* Test hook: LL consumers wait for flag + value, which no producer ever
+     * writes when value != 0, so every wait times out.  Default 0. */
+    arOptDebugFlagSkew = 4,
+    /* HB: 16-byte vectors each lane handles per rank per step (1, 2 or 4);
+     * 0 = default. */
+    arOptHBUnroll = 5,
+    /* LL: threads per workgroup (64, 128, 256, 512 or 1024); 0 = default. */
+    arOptLLThreads = 6
+} arOption_t;
+
+/* Create a communicator on `device` for groups of up to `maxRanks` (1..32)
+ * simulated ranks and LL messages of up to `maxLLBytesPerRank` bytes per rank.
+ * It owns device memory for the LL packets (2 * maxRanks * maxLLBytesPerRank
+ * bytes, each 4-byte payload travels in an 8-byte packet) and a few control
+ * words (the packet epoch, a workgroup ticket, the asynchronous error).
+ * maxLLBytesPerRank may be 0 (HB only).  Allocates with hipMalloc, so it must
+ * not be called while a stream is being captured.  The caller's current
+ * device is left unchanged.
+ * Returns arInvalidArgument for a NULL `comm` or out-of-range sizes,
+ * arHipError if the device or memory is not available. */
+arResult_t arCommCreate(arComm_t *comm, int device, int maxRanks, size_t maxLLBytesPerRank);
+
+/* Free the communicator.  Work that uses it must have finished. */
+arResult_t arCommDestroy(arComm_t comm);
+
+/* Enqueue, on `stream`, a kernel that clears the LL packets, the epoch and the
+ * asynchronous error, so that the communicator can be used again after a
+ * timeout.  No allocation and no memset node: safe to capture in a graph. */
+arResult_t arCommReset(arComm_t comm, arStream_t stream);
+
+/* Read the asynchronous error recorded by earlier kernels: arSuccess or
+ * arTimeout.  Synchronises the device first.  The error stays set until
+ * arCommReset. */
+arResult_t arCommGetAsyncError(arComm_t comm, arResult_t *asyncError);
+
+/* Set or read one option (arOption_t) of the communicator.  Values outside an
+ * option's range give arInvalidArgument. */
+arResult_t arCommSetOption(arComm_t comm, arOption_t option, int64_t value);
+arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
+
+/* The sum all-reduce.
+ *
+ *  sendbufs  host array of `nranks` device pointers; sendbufs[r] holds rank
+ *            r's `count` elements, contiguous.  Read only during the call.
+ *  recvbufs  host array of `nranks` device pointers for the results, laid
+ *            out like sendbufs.  recvbufs[r] == sendbufs[r] for a rank means
+ *            in place; the result is then computed from the values the
+ *            buffers held when the kernel started.
+ *  count     elements per rank.  0 returns arSuccess and enqueues nothing.
+ *  dtype     arBfloat16, arFloat16 or arFloat32 (else arUnsupported).
+ *  op        arSum only (else arUnsupported).
+ *  nranks    1..32 (else arUnsupported); 1 is a copy.
+ *  protocol  arProtoLL or arProtoHB (else arInvalidArgument).
+ *  comm      a communicator on the current device.
+ *  stream    the stream to enqueue on.
+ *
+ * Rules (arInvalidArgument when broken): no NULL pointer; every pointer
+ * 16-byte aligned; the 2*nranks byte ranges do not overlap except that a
+ * receive buffer may coincide exactly with the same rank's send buffer, and
+ * send buffers may overlap one another (they are only read).
+ * LL also needs nranks <= the communicator's maxRanks and count * element
+ * size <= its maxLLBytesPerRank (arInvalidUsage otherwise).
+ *
+ * The call only enqueues work and returns; the buffers belong to the caller
+ * and must stay valid until the work has run (for a captured graph, as long
+ * as the graph is replayed).  Nothing is allocated or synchronised, so calls
+ * can be captured into a HIP graph.  Validation makes no HIP call, so every
+ * argument error is reported without touching the device. */
+arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_t count,
+                       arDataType_t dtype, arRedOp_t op, int nranks, arProtocol_t protocol,
+                       arComm_t comm, arStream_t stream);
+
+/* Static description of a result code. */
+const char *arGetErrorString(arResult_t result);
+
+/* AR_VERSION of the built library. */
+int arGetVersion(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AR_ALLREDUCE_H */

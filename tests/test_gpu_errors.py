@@ -1,0 +1,67 @@
+"""Error paths on the GPU, forced from the host so every kernel still exits.
+
+An LL wait is bounded; a communicator option makes the consumers wait for a
+flag value no producer writes, with a 2 ms bound, so each wait runs out,
+records arTimeout and the kernel finishes.  arCommReset then clears the state
+and the next call is correct again.
+"""
+import pytest
+import torch
+
+import all_reduce_amd as ar
+from all_reduce_amd import inputs
+from gpu_util import assert_parity, expect, note, run_allreduce
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture()
+def comm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    c = ar.Comm(device="cuda:0", max_ranks=8, max_ll_bytes_per_rank=1 << 16)
+    yield c
+    c.close()
+
+
+def test_forced_timeout_is_reported_then_reset_recovers(comm, orc):
+    x = inputs.make(8, 4096, "bf16", "uniform", seed=51)
+    assert comm.async_error() == ar.arResult.arSuccess
+    comm.set_option(ar.arOption.arOptPollTimeoutUs, 2000)
+    comm.set_option(ar.arOption.arOptDebugFlagSkew, 1)
+    note("LL with a flag no producer writes (2 ms bound)")
+    run_allreduce(comm, x, "ll")
+    assert comm.async_error() == ar.arResult.arTimeout
+    comm.set_option(ar.arOption.arOptDebugFlagSkew, 0)
+    # the error is sticky until reset
+    run_allreduce(comm, x, "hb")
+    assert comm.async_error() == ar.arResult.arTimeout
+    comm.reset()
+    assert comm.async_error() == ar.arResult.arSuccess
+    note("LL after reset")
+    assert_parity(run_allreduce(comm, x, "ll"), expect(orc, x), "after reset")
+    assert comm.async_error() == ar.arResult.arSuccess
+
+
+def test_limits_of_the_communicator(comm):
+    x = torch.zeros((8, (1 << 16) // 2 + 8), dtype=torch.bfloat16, device="cuda")
+    ptrs = [t.data_ptr() for t in x]
+    s = torch.cuda.current_stream().cuda_stream
+    # LL above maxLLBytesPerRank, and more ranks than the communicator holds
+    assert ar.arAllReduce(ptrs, ptrs, x.shape[1], 0, 0, 8, 0, comm.handle, s) == \
+        ar.arResult.arInvalidUsage
+    y = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
+    p16 = [t.data_ptr() for t in y]
+    assert ar.arAllReduce(p16, p16, 64, 0, 0, 16, 0, comm.handle, s) == ar.arResult.arInvalidUsage
+    # HB has no such limits
+    assert ar.arAllReduce(p16, p16, 64, 0, 0, 16, 1, comm.handle, s) == ar.arResult.arSuccess
+    torch.cuda.synchronize()
+
+
+def test_option_ranges(comm):
+    with pytest.raises(ar.ArError):
+        comm.set_option(ar.arOption.arOptHBUnroll, 3)
+    with pytest.raises(ar.ArError):
+        comm.set_option(ar.arOption.arOptLLThreads, 96)
+    comm.set_option(ar.arOption.arOptHBUnroll, 4)
+    assert comm.get_option(ar.arOption.arOptHBUnroll) == 4

@@ -1,0 +1,80 @@
+"""Calls captured in a HIP graph and replayed (through torch.cuda.CUDAGraph).
+
+Replays freeze the kernel arguments, so the LL packet flags must come from the
+device-side epoch: two inputs alternating in one graph would read each other's
+stale packets otherwise.  Every replay is checked against the oracle, with
+eager calls and synchronisations between replays.
+"""
+import pytest
+import torch
+
+import all_reduce_amd as ar
+from all_reduce_amd import inputs
+from gpu_util import CODES, PROTO, assert_parity, expect, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def comm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    c = ar.Comm(device="cuda:0", max_ranks=32, max_ll_bytes_per_rank=1 << 20)
+    yield c
+    c.close()
+
+
+def call(comm, sv, rv, n, dtype, protocol):
+    rc = ar.arAllReduce([t.data_ptr() for t in sv], [t.data_ptr() for t in rv], n,
+                        CODES[dtype], ar.arRedOp.arSum, len(sv), PROTO[protocol], comm.handle,
+                        torch.cuda.current_stream().cuda_stream)
+    assert rc == ar.arResult.arSuccess, ar.arGetErrorString(rc)
+
+
+@pytest.mark.parametrize("protocol", ["ll", "hb"])
+@pytest.mark.parametrize("N", [1024, 65536 + 3, 1 << 19])
+def test_graph_alternating_inputs(comm, orc, protocol, N):
+    R, dt = 8, "bf16"
+    xa = inputs.make(R, N, dt, "uniform", seed=41)
+    xb = inputs.make(R, N, dt, "uniform", seed=42)
+    want_a, want_b = expect(orc, xa), expect(orc, xb)
+    _, sa = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    _, sb = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    pa, da = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    pb, db = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    for r in range(R):
+        sa[r].copy_(xa[r])
+        sb[r].copy_(xb[r])
+    note(f"graph {protocol} N={N}: warm-up")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            call(comm, sa, da, N, dt, protocol)
+            call(comm, sb, db, N, dt, protocol)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    note(f"graph {protocol} N={N}: capture 10 calls")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(10):
+            if i % 2 == 0:
+                call(comm, sa, da, N, dt, protocol)
+            else:
+                call(comm, sb, db, N, dt, protocol)
+    torch.cuda.synchronize()
+
+    x_small = inputs.make(R, 777, dt, "normal", seed=43)
+    for rep in range(4):
+        note(f"graph {protocol} N={N}: replay {rep}")
+        pa.view(torch.uint8).fill_(0xA5)
+        pb.view(torch.uint8).fill_(0x5A)
+        g.replay()
+        torch.cuda.synchronize()
+        assert_parity(torch.stack([t.cpu() for t in da]), want_a, f"replay {rep} A")
+        assert_parity(torch.stack([t.cpu() for t in db]), want_b, f"replay {rep} B")
+        # eager work of another size between replays advances the epoch too
+        from gpu_util import run_allreduce
+        assert_parity(run_allreduce(comm, x_small, protocol), expect(orc, x_small), "eager")
+    assert comm.async_error() == ar.arResult.arSuccess

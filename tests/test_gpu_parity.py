@@ -1,0 +1,204 @@
+"""GPU parity: the HIP all-reduce, called through the C ABI, against the oracle.
+
+The bar is bit-exact equality (NaNs by class): the kernels sum in the same
+rank order 0..R-1 in binary32 and round once with RNE, like the oracle.
+Inputs come from ``all_reduce_amd.inputs`` (seeded), never from the GPU path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import all_reduce_amd as ar
+import exact_model as em
+import pins
+from all_reduce_amd import inputs
+from gpu_util import assert_parity, bits, expect, from_bits, run_allreduce
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def comm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    c = ar.Comm(device="cuda:0", max_ranks=32, max_ll_bytes_per_rank=1 << 20)
+    yield c
+    c.close()
+
+
+def check(comm, orc, x, protocol, inplace=False, what=""):
+    got = run_allreduce(comm, x, protocol, inplace=inplace)
+    assert_parity(got, expect(orc, x), what or f"{protocol} {tuple(x.shape)} {x.dtype}")
+    return got
+
+
+# ---- the named workloads ----------------------------------------------------
+@pytest.mark.parametrize("protocol", ["ll", "hb"])
+def test_c1_small_bf16(comm, orc, protocol):
+    x = inputs.make(**inputs.WORKLOADS["C1"])
+    check(comm, orc, x, protocol)
+
+
+@pytest.mark.parametrize("k", range(10, 20))
+@pytest.mark.parametrize("protocol", ["ll", "hb"])
+def test_c2_message_sweep(comm, orc, k, protocol):
+    x = inputs.make(**inputs.sweep(k))
+    check(comm, orc, x, protocol)
+
+
+def test_c3_decode_ll_and_hb_agree(comm, orc):
+    x = inputs.make(**inputs.WORKLOADS["C3"])
+    a = check(comm, orc, x, "ll")
+    b = check(comm, orc, x, "hb")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_c4_prefill_in_place_full_size(comm, orc):
+    """8 x 64M bf16 with 0.1% outliers, in place, checked element by element."""
+    x = inputs.make(**inputs.WORKLOADS["C4"])
+    want = expect(orc, x)
+    got = run_allreduce(comm, x, "hb", inplace=True)
+    assert_parity(got, want, "C4 in place")
+    # the outliers make the result order-sensitive, so this parity checks the order
+    rev = orc.allreduce(bits(x.flip(0)), "bf16", nthreads=16)
+    assert int((rev[0] != want[0]).sum()) > 0
+
+
+@pytest.mark.parametrize("R", [16, 32])
+def test_c5_fp16_integer_sums(comm, orc, R):
+    case = inputs.integer_case(R, "fp16")
+    x = inputs.make(**case)
+    got = check(comm, orc, x, "hb")
+    exact = x.to(torch.int64).sum(0)
+    assert torch.equal(got[0].to(torch.int64), exact)
+
+
+@pytest.mark.parametrize("R", [16, 32])
+def test_c5_fp32_integer_sums_full_size(comm, orc, R):
+    """R x 4096*7168 fp32: exact integer sums everywhere, oracle on a sample."""
+    case = inputs.integer_case(R, "fp32")
+    x = inputs.make(**case)
+    got = run_allreduce(comm, x, "hb")
+    exact = x.to(torch.int64).sum(0)
+    for r in range(R):
+        assert torch.equal(got[r].to(torch.int64), exact), f"rank {r}"
+    g = torch.Generator().manual_seed(99)
+    idx = torch.randint(0, x.shape[1], (1 << 20,), generator=g)
+    want = expect(orc, x[:, idx].contiguous())
+    assert_parity(got[:, idx].contiguous(), want, f"C5 fp32 R={R} sampled")
+
+
+# ---- shapes, tails and rank counts --------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 13, 16, 32])
+@pytest.mark.parametrize("N", [1, 2, 3, 7, 9, 1023, 1025, 65536 + 5])
+@pytest.mark.parametrize("protocol", ["ll", "hb"])
+def test_tails_and_rank_counts(comm, orc, dtype, R, N, protocol):
+    x = inputs.make(R, N, dtype, "normal", seed=1000 + R * 31 + N)
+    check(comm, orc, x, protocol)
+
+
+@pytest.mark.parametrize("protocol", ["ll", "hb"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_several_hb_tiles_and_ragged_chunks(comm, orc, protocol, dtype):
+    # spans many tiles per chunk; N % R != 0 and N % 8 != 0
+    x = inputs.make(8, 3 * 262144 + 12345, dtype, "outliers", seed=21)
+    if protocol == "ll":
+        x = x[:, : (1 << 20) // x.element_size()].contiguous()
+    check(comm, orc, x, protocol)
+
+
+@pytest.mark.parametrize("protocol", ["ll", "hb"])
+def test_in_place_equals_out_of_place(comm, orc, protocol):
+    x = inputs.make(8, 100_000, "bf16", "normal", seed=7)
+    a = run_allreduce(comm, x, protocol)
+    b = run_allreduce(comm, x, protocol, inplace=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert_parity(b, expect(orc, x), "in place")
+
+
+@pytest.mark.parametrize("protocol", ["ll", "hb"])
+def test_repeat_is_bitwise_deterministic(comm, protocol):
+    x = inputs.make(8, 300_001, "fp16", "normal", seed=8)
+    a = run_allreduce(comm, x, protocol)
+    b = run_allreduce(comm, x, protocol)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---- special values --------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("protocol", ["ll", "hb"])
+def test_exhaustive_value_set_three_ranks(comm, protocol, dtype):
+    """Every 3-rank column over the signed-zero/subnormal/tie/inf/NaN value set,
+    against the exact rational model."""
+    cols, want = pins._exhaustive_cols(dtype, 3)
+    x = from_bits(pins.to_array(cols, dtype).view(np.uint32 if dtype == "fp32" else np.uint16),
+                  dtype)
+    got = run_allreduce(comm, x, protocol)
+    for r in range(3):
+        pins.assert_same_bits(bits(got[r]), want, dtype, f"value set {dtype} rank {r}")
+
+
+@pytest.mark.parametrize("protocol", ["ll", "hb"])
+def test_hand_cases(comm, protocol):
+    for dtype, ins, out in pins.load_hand_cases():
+        x = from_bits(pins.to_array([ins], dtype).view(
+            np.uint32 if dtype == "fp32" else np.uint16), dtype)
+        got = run_allreduce(comm, x, protocol)
+        for r in range(len(ins)):
+            pins.assert_same_bits(bits(got[r]), np.array([out]), dtype,
+                                  f"hand case {dtype} {[hex(v) for v in ins]}")
+
+
+@pytest.mark.parametrize("protocol", ["ll", "hb"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_signed_zeros_and_one_hot(comm, protocol, dtype):
+    R, N = 8, 4096
+    fmt = em.FORMATS[dtype]
+    top = fmt.ebits + fmt.mbits
+    npdt = np.uint32 if dtype == "fp32" else np.uint16
+    neg = np.full((R, N), 1 << top, dtype=npdt)
+    got = bits(run_allreduce(comm, from_bits(neg, dtype), protocol))
+    assert np.all(got == (1 << top)), "all -0 must give -0"
+    rng = np.random.default_rng(5)
+    vals = pins.random_bits(rng, dtype, (N,), emin=-10, emax=10)
+    hot = rng.integers(0, R, N)
+    x = np.zeros((R, N), dtype=npdt)
+    x[hot, np.arange(N)] = vals
+    got = bits(run_allreduce(comm, from_bits(x, dtype), protocol))
+    for r in range(R):
+        assert np.array_equal(got[r], vals)
+
+
+# ---- launch configurations do not change the bits -----------------------------
+@pytest.mark.parametrize("opt,values", [
+    (ar.arOption.arOptHBUnroll, [1, 2, 4]),
+    (ar.arOption.arOptHBNonTemporal, [0, 1]),
+    (ar.arOption.arOptHBBlocksPerCU, [1, 2, 8]),
+])
+def test_hb_tuning_options_keep_bits(comm, orc, opt, values):
+    x = inputs.make(8, 1_000_003, "bf16", "outliers", seed=31)
+    want = expect(orc, x)
+    old = comm.get_option(opt)
+    try:
+        for v in values:
+            comm.set_option(opt, v)
+            assert_parity(run_allreduce(comm, x, "hb"), want, f"{opt.name}={v}")
+    finally:
+        comm.set_option(opt, old)
+
+
+@pytest.mark.parametrize("opt,values", [
+    (ar.arOption.arOptLLThreads, [64, 128, 512, 1024]),
+    (ar.arOption.arOptLLBlocksPerRank, [1, 3, 16, 64]),
+])
+def test_ll_tuning_options_keep_bits(comm, orc, opt, values):
+    x = inputs.make(8, 200_003, "bf16", "outliers", seed=32)
+    want = expect(orc, x)
+    old = comm.get_option(opt)
+    try:
+        for v in values:
+            comm.set_option(opt, v)
+            assert_parity(run_allreduce(comm, x, "ll"), want, f"{opt.name}={v}")
+    finally:
+        comm.set_option(opt, old)
