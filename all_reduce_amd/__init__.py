@@ -47,11 +47,13 @@ class arProtocol(IntEnum):
 class arOption(IntEnum):
     arOptPollTimeoutUs = 0
     arOptLLBlocksPerRank = 1
-    arOptHBBlocksPerCU = 2
+    arOptHBBlocks = 2
     arOptHBNonTemporal = 3
     arOptDebugFlagSkew = 4
     arOptHBUnroll = 5
     arOptLLThreads = 6
+    arOptHBThreads = 7
+    arOptHBChunkLayout = 8
 
 
 AR_MAX_RANKS = 32

@@ -49,14 +49,16 @@ bool overlaps(uintptr_t a, uintptr_t b, size_t len)
     return a < b + len && b < a + len;
 }
 
-constexpr int64_t kDefaults[7] = {
+constexpr int64_t kDefaults[kOptionCount] = {
     2000000,  // arOptPollTimeoutUs
     0,        // arOptLLBlocksPerRank (auto)
-    0,        // arOptHBBlocksPerCU (auto)
+    0,        // arOptHBBlocks (auto)
     1,        // arOptHBNonTemporal
     0,        // arOptDebugFlagSkew
     0,        // arOptHBUnroll (auto)
     0,        // arOptLLThreads (auto)
+    0,        // arOptHBThreads (auto)
+    1,        // arOptHBChunkLayout (interleaved tiles)
 };
 
 // Argument checks shared by every protocol.  No HIP call.
@@ -251,7 +253,7 @@ arResult_t arCommSetOption(arComm_t comm, arOption_t option, int64_t value)
     switch (option) {
     case arOptPollTimeoutUs: ok = value >= 1 && value <= 600000000; break;
     case arOptLLBlocksPerRank: ok = value >= 0 && value <= 65536; break;
-    case arOptHBBlocksPerCU: ok = value >= 0 && value <= 64; break;
+    case arOptHBBlocks: ok = value >= 0 && value <= (1 << 20); break;
     case arOptHBNonTemporal: ok = value == 0 || value == 1; break;
     case arOptDebugFlagSkew: ok = value >= 0 && value <= 65535; break;
     case arOptHBUnroll: ok = value == 0 || value == 1 || value == 2 || value == 4; break;
@@ -259,6 +261,8 @@ arResult_t arCommSetOption(arComm_t comm, arOption_t option, int64_t value)
         ok = value == 0 || value == 64 || value == 128 || value == 256 || value == 512 ||
              value == 1024;
         break;
+    case arOptHBThreads: ok = value >= 0 && value <= 1024 && value % 64 == 0; break;
+    case arOptHBChunkLayout: ok = value == 0 || value == 1; break;
     default: return reject(arInvalidArgument, "unknown option");
     }
     if (!ok)
@@ -271,7 +275,7 @@ arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value)
 {
     if (comm == nullptr || value == nullptr)
         return reject(arInvalidArgument, "NULL argument");
-    if ((int)option < 0 || (int)option >= (int)(sizeof(kDefaults) / sizeof(kDefaults[0])))
+    if ((int)option < 0 || (int)option >= kOptionCount)
         return reject(arInvalidArgument, "unknown option");
     *value = comm->opt[option];
     return arSuccess;

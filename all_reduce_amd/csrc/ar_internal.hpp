@@ -28,7 +28,7 @@ struct HBParams {
     uint32_t blocks_per_chunk;
     uint32_t nranks;      // runtime rank count (the generic kernel; else == R)
     uint32_t tail_elems;  // elements after the last whole vector
-    uint32_t pad;
+    uint32_t interleaved; // 0: chunk c = contiguous vectors; 1: tiles c, c+R, c+2R, ...
 };
 
 // One-shot LL launch parameters.
@@ -58,6 +58,8 @@ constexpr int kThreadChoices = 5; // 64, 128, 256, 512, 1024
 
 }  // namespace ar
 
+constexpr int kOptionCount = 9;
+
 struct arComm {
     int device;
     int max_ranks;
@@ -67,7 +69,7 @@ struct arComm {
     uint64_t *pkts;        // 2 * max_ranks * max_ll_bytes bytes
     uint64_t pkt_stride;   // packets per rank region
     uint32_t *ctrl;        // 64 bytes of control words
-    int64_t opt[7];        // indexed by arOption_t
+    int64_t opt[kOptionCount]; // indexed by arOption_t
     int ll_resident[3][ar::kRankVariants + 1][ar::kThreadChoices];
 };
 

@@ -27,8 +27,6 @@
 
 namespace ar {
 
-constexpr int kHBThreads = 256;
-
 // Scalar path for the elements after the last whole 16-byte vector.
 template <typename T>
 __device__ inline float load_elem(const void *base, uint64_t i)
@@ -52,27 +50,43 @@ __device__ inline void store_elem(void *base, uint64_t i, float a)
         ((uint32_t *)base)[i] = w;
 }
 
+// Largest workgroup compiled for a rank-table size: the R 16-byte vectors a
+// lane holds (4 VGPRs each) must fit the register share of that many threads.
+constexpr int hb_max_threads(int rmax) { return rmax >= 32 ? 256 : (rmax >= 16 ? 512 : 1024); }
+
 // RMAX: size of the rank table.  EXACT: nranks == RMAX at compile time;
 // otherwise nranks < RMAX arrives at run time and ranks >= nranks are skipped.
 // U: 16-byte vectors per lane per rank in flight.  NT: non-temporal access.
+// The workgroup size is a launch parameter (a tile is blockDim.x * U vectors).
 template <typename T, int RMAX, bool EXACT, int U, bool NT>
-__global__ __launch_bounds__(kHBThreads) void hb_twoshot(HBParams<RMAX> p)
+__global__ __launch_bounds__(hb_max_threads(RMAX)) void hb_twoshot(HBParams<RMAX> p)
 {
     const uint32_t n = EXACT ? RMAX : p.nranks;
+    const uint32_t nthr = blockDim.x;
     const uint32_t c = blockIdx.x % n;       // chunk, and the simulated rank owning it
     const uint32_t bb = blockIdx.x / n;      // this workgroup's place among the chunk's
-    const uint64_t c0 = (uint64_t)c * p.chunk_vec;
-    const uint64_t c1 = (c == n - 1) ? p.nvec : c0 + p.chunk_vec;
-    const uint64_t tile = (uint64_t)kHBThreads * U;
-    const uint64_t stride = (uint64_t)p.blocks_per_chunk * tile;
+    const uint64_t tile = (uint64_t)nthr * U;
+    // Chunk c is either the contiguous vectors [c*C, (c+1)*C) (the last chunk
+    // takes the rest) or, interleaved, every tile whose index is c modulo n.
+    uint64_t start, step, end;
+    if (p.interleaved) {
+        start = ((uint64_t)bb * n + c) * tile;
+        step = (uint64_t)p.blocks_per_chunk * n * tile;
+        end = p.nvec;
+    } else {
+        const uint64_t c0 = (uint64_t)c * p.chunk_vec;
+        start = c0 + (uint64_t)bb * tile;
+        step = (uint64_t)p.blocks_per_chunk * tile;
+        end = (c == n - 1) ? p.nvec : c0 + p.chunk_vec;
+    }
 
-    for (uint64_t base = c0 + (uint64_t)bb * tile; base < c1; base += stride) {
+    for (uint64_t base = start; base < end; base += step) {
         u32x4 v[U][RMAX];
         // reduce-scatter: every load of the tile is issued before any use
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint64_t i = base + (uint64_t)u * kHBThreads + threadIdx.x;
-            if (i < c1) {
+            const uint64_t i = base + (uint64_t)u * nthr + threadIdx.x;
+            if (i < end) {
 #pragma unroll
                 for (int j = 0; j < RMAX; ++j)
                     if (EXACT || j < (int)n)
@@ -81,8 +95,8 @@ __global__ __launch_bounds__(kHBThreads) void hb_twoshot(HBParams<RMAX> p)
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint64_t i = base + (uint64_t)u * kHBThreads + threadIdx.x;
-            if (i < c1) {
+            const uint64_t i = base + (uint64_t)u * nthr + threadIdx.x;
+            if (i < end) {
                 u32x4 y;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -123,31 +137,29 @@ __global__ __launch_bounds__(kHBThreads) void hb_twoshot(HBParams<RMAX> p)
 namespace {
 
 template <typename T, int RMAX, bool EXACT, int U, bool NT>
-hipError_t launch_one(const HBParams<RMAX> &p, uint32_t grid, hipStream_t stream)
+hipError_t launch_one(const HBParams<RMAX> &p, uint32_t grid, uint32_t threads, hipStream_t stream)
 {
-    hipLaunchKernelGGL((hb_twoshot<T, RMAX, EXACT, U, NT>), dim3(grid), dim3(kHBThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((hb_twoshot<T, RMAX, EXACT, U, NT>), dim3(grid), dim3(threads), 0, stream, p);
     return hipGetLastError();
 }
 
 // Largest vectors-per-lane count compiled for a rank table size (register
 // budget: U * RMAX * 4 VGPRs of loaded data per lane).
-constexpr int max_unroll(int rmax) { return rmax <= 8 ? 4 : (rmax <= 16 ? 2 : 1); }
+constexpr int max_unroll(int rmax) { return rmax <= 4 ? 4 : (rmax <= 8 ? 2 : 1); }
 
 template <typename T, int RMAX, bool EXACT>
-hipError_t launch_unroll(const HBParams<RMAX> &p, uint32_t grid, int unroll, bool nt,
-                         hipStream_t stream)
+hipError_t launch_unroll(const HBParams<RMAX> &p, uint32_t grid, uint32_t threads, int u,
+                         bool nt, hipStream_t stream)
 {
     constexpr int kMax = max_unroll(RMAX);
-    int u = unroll > kMax ? kMax : unroll;
     if (u >= 4 && kMax >= 4)
-        return nt ? launch_one<T, RMAX, EXACT, (kMax >= 4 ? 4 : 1), true>(p, grid, stream)
-                  : launch_one<T, RMAX, EXACT, (kMax >= 4 ? 4 : 1), false>(p, grid, stream);
+        return nt ? launch_one<T, RMAX, EXACT, (kMax >= 4 ? 4 : 1), true>(p, grid, threads, stream)
+                  : launch_one<T, RMAX, EXACT, (kMax >= 4 ? 4 : 1), false>(p, grid, threads, stream);
     if (u >= 2 && kMax >= 2)
-        return nt ? launch_one<T, RMAX, EXACT, (kMax >= 2 ? 2 : 1), true>(p, grid, stream)
-                  : launch_one<T, RMAX, EXACT, (kMax >= 2 ? 2 : 1), false>(p, grid, stream);
-    return nt ? launch_one<T, RMAX, EXACT, 1, true>(p, grid, stream)
-              : launch_one<T, RMAX, EXACT, 1, false>(p, grid, stream);
+        return nt ? launch_one<T, RMAX, EXACT, (kMax >= 2 ? 2 : 1), true>(p, grid, threads, stream)
+                  : launch_one<T, RMAX, EXACT, (kMax >= 2 ? 2 : 1), false>(p, grid, threads, stream);
+    return nt ? launch_one<T, RMAX, EXACT, 1, true>(p, grid, threads, stream)
+              : launch_one<T, RMAX, EXACT, 1, false>(p, grid, threads, stream);
 }
 
 template <typename T, int RMAX, bool EXACT>
@@ -164,25 +176,32 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     p.tail_elems = (uint32_t)(count % kPerVec);
     p.chunk_vec = p.nvec / (uint64_t)nranks;
     p.nranks = (uint32_t)nranks;
+    p.interleaved = comm->opt[arOptHBChunkLayout] == 1 ? 1u : 0u;
 
-    const int unroll = comm->opt[arOptHBUnroll] > 0 ? (int)comm->opt[arOptHBUnroll] : 2;
+    int u = comm->opt[arOptHBUnroll] > 0 ? (int)comm->opt[arOptHBUnroll] : 1;
+    if (u > max_unroll(RMAX))
+        u = max_unroll(RMAX);
     const bool nt = comm->opt[arOptHBNonTemporal] != 0;
-    const int per_cu = comm->opt[arOptHBBlocksPerCU] > 0 ? (int)comm->opt[arOptHBBlocksPerCU] : 4;
-    const int u_eff = unroll > max_unroll(RMAX) ? max_unroll(RMAX) : unroll;
+    uint32_t threads = comm->opt[arOptHBThreads] > 0 ? (uint32_t)comm->opt[arOptHBThreads] : 256u;
+    if (threads > (uint32_t)hb_max_threads(RMAX))
+        threads = (uint32_t)hb_max_threads(RMAX);
+    const uint64_t blocks = comm->opt[arOptHBBlocks] > 0 ? (uint64_t)comm->opt[arOptHBBlocks]
+                                                         : (uint64_t)comm->cu_count;
 
-    // Enough workgroups to fill the chip, but never more than the largest
-    // chunk has tiles.
-    const uint64_t tile = (uint64_t)kHBThreads * (uint64_t)u_eff;
-    const uint64_t last_chunk = p.nvec - p.chunk_vec * (uint64_t)(nranks - 1);
-    const uint64_t tiles = (last_chunk + tile - 1) / tile;
-    uint64_t want = ((uint64_t)comm->cu_count * (uint64_t)per_cu + (uint64_t)nranks - 1) /
-                    (uint64_t)nranks;
+    // Enough workgroups to fill the chip, but never more per chunk than the
+    // largest chunk has tiles.
+    const uint64_t tile = (uint64_t)threads * (uint64_t)u;
+    const uint64_t largest = p.interleaved
+                                 ? (p.nvec + (uint64_t)nranks - 1) / (uint64_t)nranks
+                                 : p.nvec - p.chunk_vec * (uint64_t)(nranks - 1);
+    const uint64_t tiles = (largest + tile - 1) / tile;
+    const uint64_t want = (blocks + (uint64_t)nranks - 1) / (uint64_t)nranks;
     uint64_t bpc = tiles < want ? tiles : want;
     if (bpc < 1)
         bpc = 1;
     p.blocks_per_chunk = (uint32_t)bpc;
     const uint32_t grid = (uint32_t)(bpc * (uint64_t)nranks);
-    return launch_unroll<T, RMAX, EXACT>(p, grid, unroll, nt, stream);
+    return launch_unroll<T, RMAX, EXACT>(p, grid, threads, u, nt, stream);
 }
 
 template <typename T>

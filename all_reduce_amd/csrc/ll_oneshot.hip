@@ -24,7 +24,8 @@
 //
 // Flags come from an epoch counter in device memory, so replaying a captured
 // graph (whose kernel arguments are frozen) still gives every call a new flag;
-// the last workgroup to finish advances it.  Flag 0 is never used, so cleared
+// the workgroup that takes the last ticket (every workgroup takes one once it
+// holds its copy of the flag) advances it.  Flag 0 is never used, so cleared
 // packet memory never looks ready.  A wait is bounded by a wall-clock limit:
 // on expiry the lane records arTimeout in the communicator and stops waiting.
 // Every workgroup of the grid must be resident at once (the host caps the
@@ -34,27 +35,88 @@
 
 namespace ar {
 
+// Largest workgroup compiled for a rank-table size (the polled packets of a
+// lane, 2 VGPRs each, must fit the register share of that many threads).
+constexpr int ll_max_threads(int rmax) { return rmax >= 32 ? 512 : 1024; }
+// Words a lane polls at once: R packets each, all loads in flight together.
+constexpr int ll_get_batch(int rmax) { return rmax <= 8 ? 2 : 1; }
+// Source words a lane loads before it stores their packets.
+constexpr int kPutBatch = 8;
+
 template <typename T, int RMAX, bool EXACT>
-__global__ __launch_bounds__(1024) void ll_oneshot(LLParams<RMAX> p)
+__global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX> p)
 {
+    constexpr int GB = ll_get_batch(RMAX);
     const uint32_t n = EXACT ? RMAX : p.nranks;
+    const uint32_t nthr = blockDim.x;
     const uint32_t k = blockIdx.x % n;
     const uint32_t b = blockIdx.x / n;
     uint32_t *ctrl = p.ctrl;
+    __shared__ uint32_t s_flag;
 
-    const uint32_t epoch = __hip_atomic_load(ctrl + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t flag = (epoch + 1u == 0u) ? 1u : epoch + 1u;
-
-    // put: publish rank k's words of slice b
+    // put: publish rank k's words of slice b.  The first batch of source
+    // loads is issued before the epoch is read, so the two latencies overlap.
     const uint64_t p0 = (uint64_t)b * p.put_per_block;
     const uint64_t p1 = (p0 + p.put_per_block < p.npkt) ? p0 + p.put_per_block : p.npkt;
     const uint32_t *src = (const uint32_t *)p.rk.send[k];
     uint64_t *mine = p.pkts + (uint64_t)k * p.pkt_stride;
-    for (uint64_t q = p0 + threadIdx.x; q < p1; q += blockDim.x) {
-        uint32_t w = (p.half_tail && q == p.npkt - 1) ? (uint32_t)((const uint16_t *)(src + q))[0]
-                                                      : src[q];
-        put_packet(mine + q, w, flag);
+    // Whole 4-byte words go through the batches; a message of odd 16-bit
+    // length ends in one 2-byte word, handled by a single lane below.
+    const uint64_t nfull = p.npkt - p.half_tail;
+    const uint64_t pf = p1 < nfull ? p1 : nfull;
+    const uint64_t pstep = (uint64_t)kPutBatch * nthr;
+    uint64_t pbase = p0 + threadIdx.x;
+    uint32_t w[kPutBatch];
+#pragma unroll
+    for (int v = 0; v < kPutBatch; ++v) {
+        const uint64_t q = pbase + (uint64_t)v * nthr;
+        if (q < pf)
+            w[v] = src[q];
     }
+    if (threadIdx.x == 0) {
+        const uint32_t epoch =
+            __hip_atomic_load(ctrl + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_flag = (epoch + 1u == 0u) ? 1u : epoch + 1u;
+    }
+    __syncthreads();
+    const uint32_t flag = s_flag;
+
+    // gfx9 counts loads and stores on one counter that runs out of order
+    // once both are pending, so a load result needed after a store forces a
+    // wait for everything.  One explicit wait here (the loads were in flight
+    // during the epoch read) lets the batch's stores issue back to back.
+    __builtin_amdgcn_s_waitcnt(0);
+
+    for (;;) {
+#pragma unroll
+        for (int v = 0; v < kPutBatch; ++v) {
+            const uint64_t q = pbase + (uint64_t)v * nthr;
+            if (q < pf)
+                put_packet(mine + q, w[v], flag);
+        }
+        pbase += pstep;
+        if (pbase >= pf)
+            break;
+#pragma unroll
+        for (int v = 0; v < kPutBatch; ++v) {
+            const uint64_t q = pbase + (uint64_t)v * nthr;
+            if (q < pf)
+                w[v] = src[q];
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    if (p.half_tail && threadIdx.x == 0 && nfull >= p0 && nfull < p1)
+        put_packet(mine + nfull, (uint32_t)((const uint16_t *)(src + nfull))[0], flag);
+
+    // This workgroup holds its copy of the flag, so it can take its ticket;
+    // it does so after its packets are on their way, so that no packet store
+    // waits for the atomic.  The workgroup that takes the last ticket knows
+    // every workgroup has read the epoch and advances it for the next call;
+    // consumers still waiting compare against their own copy.  Relaxed is
+    // enough: the next call reads the epoch only after this kernel has ended.
+    uint32_t ticket = 0;
+    if (threadIdx.x == 0)
+        ticket = __hip_atomic_fetch_add(ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // poll, reduce, output: sub-slice k of slice b
     uint32_t want = flag + p.flag_skew;
@@ -70,18 +132,27 @@ __global__ __launch_bounds__(1024) void ll_oneshot(LLParams<RMAX> p)
     uint64_t spins = 0;
     const uint64_t spin_limit = p.timeout_ticks;
     bool gave_up = false;
-    for (uint64_t q = g0 + threadIdx.x; q < g1 && !gave_up; q += blockDim.x) {
-        uint64_t pk[RMAX];
+    for (uint64_t q0 = g0 + threadIdx.x; q0 < g1 && !gave_up; q0 += (uint64_t)GB * nthr) {
+        uint64_t pk[GB][RMAX];
 #pragma unroll
-        for (int j = 0; j < RMAX; ++j)
-            if (EXACT || j < (int)n)
-                pk[j] = read_packet(p.pkts + (uint64_t)j * p.pkt_stride + q);
+        for (int v = 0; v < GB; ++v) {
+            const uint64_t q = q0 + (uint64_t)v * nthr;
+            if (q < g1) {
+#pragma unroll
+                for (int j = 0; j < RMAX; ++j)
+                    if (EXACT || j < (int)n)
+                        pk[v][j] = read_packet(p.pkts + (uint64_t)j * p.pkt_stride + q);
+            }
+        }
         for (;;) {
             bool ready = true;
 #pragma unroll
-            for (int j = 0; j < RMAX; ++j)
-                if (EXACT || j < (int)n)
-                    ready = ready && packet_flag(pk[j]) == want;
+            for (int v = 0; v < GB; ++v)
+                if (q0 + (uint64_t)v * nthr < g1)
+#pragma unroll
+                    for (int j = 0; j < RMAX; ++j)
+                        if (EXACT || j < (int)n)
+                            ready = ready && packet_flag(pk[v][j]) == want;
             if (ready)
                 break;
             const uint64_t now = wall_clock64();
@@ -94,48 +165,54 @@ __global__ __launch_bounds__(1024) void ll_oneshot(LLParams<RMAX> p)
                 break;
             }
 #pragma unroll
-            for (int j = 0; j < RMAX; ++j)
-                if ((EXACT || j < (int)n) && packet_flag(pk[j]) != want)
-                    pk[j] = read_packet(p.pkts + (uint64_t)j * p.pkt_stride + q);
+            for (int v = 0; v < GB; ++v) {
+                const uint64_t q = q0 + (uint64_t)v * nthr;
+                if (q < g1) {
+#pragma unroll
+                    for (int j = 0; j < RMAX; ++j)
+                        if ((EXACT || j < (int)n) && packet_flag(pk[v][j]) != want)
+                            pk[v][j] = read_packet(p.pkts + (uint64_t)j * p.pkt_stride + q);
+                }
+            }
         }
         if (gave_up)
             break;
 
-        float acc[T::kPerWord];
-        T::widen(packet_payload(pk[0]), acc);
 #pragma unroll
-        for (int j = 1; j < RMAX; ++j) {
-            if (EXACT || j < (int)n) {
-                float x[T::kPerWord];
-                T::widen(packet_payload(pk[j]), x);
+        for (int v = 0; v < GB; ++v) {
+            const uint64_t q = q0 + (uint64_t)v * nthr;
+            if (q >= g1)
+                continue;
+            float acc[T::kPerWord];
+            T::widen(packet_payload(pk[v][0]), acc);
 #pragma unroll
-                for (int e = 0; e < T::kPerWord; ++e)
-                    acc[e] = acc[e] + x[e];
+            for (int j = 1; j < RMAX; ++j) {
+                if (EXACT || j < (int)n) {
+                    float x[T::kPerWord];
+                    T::widen(packet_payload(pk[v][j]), x);
+#pragma unroll
+                    for (int e = 0; e < T::kPerWord; ++e)
+                        acc[e] = acc[e] + x[e];
+                }
             }
-        }
-        const uint32_t y = T::narrow(acc);
-        const bool half = p.half_tail && q == p.npkt - 1;
+            const uint32_t y = T::narrow(acc);
+            const bool half = p.half_tail && q == p.npkt - 1;
 #pragma unroll
-        for (int r = 0; r < RMAX; ++r) {
-            if (EXACT || r < (int)n) {
-                uint32_t *dst = (uint32_t *)p.rk.recv[r] + q;
-                if (half)
-                    *(uint16_t *)dst = (uint16_t)y;
-                else
-                    *dst = y;
+            for (int r = 0; r < RMAX; ++r) {
+                if (EXACT || r < (int)n) {
+                    uint32_t *dst = (uint32_t *)p.rk.recv[r] + q;
+                    if (half)
+                        *(uint16_t *)dst = (uint16_t)y;
+                    else
+                        *dst = y;
+                }
             }
         }
     }
 
-    // the last workgroup to finish advances the epoch for the next call
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t t = __hip_atomic_fetch_add(ctrl + 1, 1u, __ATOMIC_ACQ_REL,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-        if (t == gridDim.x - 1) {
-            __hip_atomic_store(ctrl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(ctrl + 0, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+    if (threadIdx.x == 0 && ticket == gridDim.x - 1) {
+        __hip_atomic_store(ctrl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ctrl + 0, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -195,7 +272,14 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     p.flag_skew = (uint32_t)comm->opt[arOptDebugFlagSkew];
     p.timeout_ticks = (uint64_t)comm->opt[arOptPollTimeoutUs] * comm->wall_clock_khz / 1000u;
 
-    const int threads = comm->opt[arOptLLThreads] > 0 ? (int)comm->opt[arOptLLThreads] : 256;
+    // Default launch shape, measured on MI355X for R = 8 bf16 from 2 KiB to
+    // 1 MiB per rank: 512-thread workgroups (1024 from 1 MiB per rank up),
+    // each publishing about 4096 words, at most 64 workgroups per rank.
+    int threads = (int)comm->opt[arOptLLThreads];
+    if (threads <= 0)
+        threads = p.npkt >= 262144 ? 1024 : 512;
+    if (threads > ll_max_threads(RMAX))
+        threads = ll_max_threads(RMAX);
     const int resident = comm->ll_resident[T::kId][variant_of(nranks)][thread_index(threads)];
     uint64_t max_per_rank = (uint64_t)(resident / nranks);
     if (max_per_rank < 1)
@@ -203,8 +287,9 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
 
     uint64_t per_rank = (uint64_t)comm->opt[arOptLLBlocksPerRank];
     if (per_rank == 0) {
-        // about eight packets per lane in the put phase
-        per_rank = (p.npkt + (uint64_t)threads * 8 - 1) / ((uint64_t)threads * 8);
+        per_rank = (p.npkt + 4095) / 4096;
+        if (per_rank > 64)
+            per_rank = 64;
     }
     if (per_rank > max_per_rank)
         per_rank = max_per_rank;
@@ -240,6 +325,10 @@ template <typename T, int RMAX, bool EXACT>
 hipError_t query_one(int *out)
 {
     for (int i = 0; i < kThreadChoices; ++i) {
+        if (kThreadOptions[i] > ll_max_threads(RMAX)) {
+            out[i] = 0;  // never launched with this many threads
+            continue;
+        }
         int per_cu = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &per_cu, reinterpret_cast<const void *>(&ll_oneshot<T, RMAX, EXACT>),

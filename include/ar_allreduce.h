@@ -69,26 +69,38 @@ typedef enum { arSum = 0 } arRedOp_t;
 
 typedef enum { arProtoLL = 0, arProtoHB = 1 } arProtocol_t;
 
-/* Tunables and test hooks, see arCommSetOption. */
+/* Tunables and test hooks, see arCommSetOption.  The launch-shape options
+ * are the (workgroups, threads per workgroup) pairs that an auto-tuner would
+ * time per message size. */
 typedef enum {
-    /* LL: longest wait for one packet, in microseconds (default 2,000,000).
-     * A wait that runs out records arTimeout in the communicator and the
-     * kernel finishes without the missing data. */
+    /* LL: longest total wait of one lane for packets, in microseconds
+     * (default 2,000,000).  A wait that runs out records arTimeout in the
+     * communicator and the kernel finishes without the missing data. */
     arOptPollTimeoutUs = 0,
     /* LL: workgroups per simulated rank; 0 = pick from the message size. */
     arOptLLBlocksPerRank = 1,
-    /* HB: workgroups per compute unit for the grid; 0 = default. */
-    arOptHBBlocksPerCU = 2,
+    /* HB: workgroups in the grid (rounded to a multiple of nranks, capped by
+     * the message's tiles); 0 = one per compute unit. */
+    arOptHBBlocks = 2,
     /* HB: 1 = non-temporal loads and stores (default), 0 = ordinary ones. */
     arOptHBNonTemporal = 3,
     /* Test hook: LL consumers wait for flag + value, which no producer ever
      * writes when value != 0, so every wait times out.  Default 0. */
     arOptDebugFlagSkew = 4,
-    /* HB: 16-byte vectors each lane handles per rank per step (1, 2 or 4);
-     * 0 = default. */
+    /* HB: 16-byte vectors each lane handles per rank per step (1, 2 or 4;
+     * capped at 2 above 4 ranks and at 1 above 8); 0 = default (1). */
     arOptHBUnroll = 5,
-    /* LL: threads per workgroup (64, 128, 256, 512 or 1024); 0 = default. */
-    arOptLLThreads = 6
+    /* LL: threads per workgroup (64, 128, 256, 512 or 1024; capped at 512
+     * above 16 ranks); 0 = default. */
+    arOptLLThreads = 6,
+    /* HB: threads per workgroup (64 .. 1024, a multiple of 64; capped at 512
+     * above 8 ranks and 256 above 16); 0 = default (256). */
+    arOptHBThreads = 7,
+    /* HB: which elements simulated rank c reduces (its chunk) -- 0: the
+     * contiguous c-th of R equal parts, 1: every R-th tile starting at tile c
+     * (default; streams all R buffers in address order, which HBM serves
+     * faster). */
+    arOptHBChunkLayout = 8
 } arOption_t;
 
 /* Create a communicator on `device` for groups of up to `maxRanks` (1..32)

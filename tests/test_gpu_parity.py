@@ -174,7 +174,9 @@ def test_signed_zeros_and_one_hot(comm, protocol, dtype):
 @pytest.mark.parametrize("opt,values", [
     (ar.arOption.arOptHBUnroll, [1, 2, 4]),
     (ar.arOption.arOptHBNonTemporal, [0, 1]),
-    (ar.arOption.arOptHBBlocksPerCU, [1, 2, 8]),
+    (ar.arOption.arOptHBBlocks, [8, 40, 256, 2048]),
+    (ar.arOption.arOptHBThreads, [64, 512, 1024]),
+    (ar.arOption.arOptHBChunkLayout, [0, 1]),
 ])
 def test_hb_tuning_options_keep_bits(comm, orc, opt, values):
     x = inputs.make(8, 1_000_003, "bf16", "outliers", seed=31)
