@@ -239,7 +239,7 @@ arResult_t arCommGetAsyncError(arComm_t comm, arResult_t *asyncError)
     DeviceGuard guard(comm->device);
     uint32_t word = 0;
     if (!guard.ok || hipDeviceSynchronize() != hipSuccess ||
-        hipMemcpy(&word, comm->ctrl + 2, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+        hipMemcpy(&word, comm->ctrl + 0, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
         return reject(arHipError, "reading the error word failed");
     *asyncError = word == 0 ? arSuccess : (arResult_t)word;
     return arSuccess;

@@ -40,7 +40,7 @@ struct LLParams {
     uint64_t npkt;           // packets per rank = ceil(bytes per rank / 4)
     uint64_t put_per_block;  // packets each workgroup publishes for its rank
     uint64_t get_per_block;  // packets each workgroup polls, reduces and writes out
-    uint32_t *ctrl;          // [0] epoch, [1] workgroup ticket, [2] async error
+    uint32_t *ctrl;          // [0] async error (0 or arTimeout)
     uint64_t timeout_ticks;  // wall-clock ticks one packet wait may take
     uint32_t flag_skew;      // test hook: consumers wait for flag + skew
     uint32_t half_tail;      // 1 when the last packet carries only 2 payload bytes
@@ -68,7 +68,7 @@ struct arComm {
     uint64_t wall_clock_khz;
     uint64_t *pkts;        // 2 * max_ranks * max_ll_bytes bytes
     uint64_t pkt_stride;   // packets per rank region
-    uint32_t *ctrl;        // 64 bytes of control words
+    uint32_t *ctrl;        // control words; [0] is the async error
     int64_t opt[kOptionCount]; // indexed by arOption_t
     int ll_resident[3][ar::kRankVariants + 1][ar::kThreadChoices];
 };

@@ -11,25 +11,33 @@
 //
 // One kernel does the whole call for all R simulated ranks.  Workgroup
 // w = b * R + k acts for rank k on slice b of the message:
-//   put     rank k's words of slice b become packets {payload, flag} in rank
+//   put     rank k's words of slice b become packets {payload, ready} in rank
 //           k's packet region (the stand-in for peer memory);
 //   poll    the workgroup takes sub-slice k of slice b and, lane by lane,
-//           re-reads the R packets of each word until all R flags carry this
-//           call's value -- R - 1 of them are written by other workgroups,
-//           which for R = 8 sit on the other seven XCDs;
+//           re-reads the R packets of each word until all R are ready --
+//           R - 1 of them are written by other workgroups, which for R = 8
+//           sit on the other seven XCDs;
 //   reduce  binary32 sum in rank order 0..R-1, rounded once to the dtype;
+//   clear   the R packets go back to zero;
 //   output  the word goes to all R receive buffers.
 // In place is safe: a word is written out only after all R packets for it
 // arrived, and each packet carries a value its producer had already read.
 //
-// Flags come from an epoch counter in device memory, so replaying a captured
-// graph (whose kernel arguments are frozen) still gives every call a new flag;
-// the workgroup that takes the last ticket (every workgroup takes one once it
-// holds its copy of the flag) advances it.  Flag 0 is never used, so cleared
-// packet memory never looks ready.  A wait is bounded by a wall-clock limit:
-// on expiry the lane records arTimeout in the communicator and stops waiting.
-// Every workgroup of the grid must be resident at once (the host caps the
-// grid with the occupancy calculator), because consumers wait on producers.
+// Packet memory is all zero between calls: every packet a call writes is
+// consumed and cleared by the same call, and the next call (on the same
+// stream, or the next node of a replayed graph) starts after this kernel has
+// ended.  So a packet is ready exactly when its flag is nonzero, and no
+// per-call sequence number is needed.  That keeps graph replays correct with
+// frozen kernel arguments and needs no shared counter: a device-wide counter
+// bumped once per workgroup costs a serialised atomic per workgroup on one
+// address, which measured about 15 ns each on MI355X (5 us for the 512
+// workgroups of a 1 MiB-per-rank call).
+// A wait is bounded by a wall-clock limit: on expiry the lane records
+// arTimeout in the communicator and stops waiting.  Packets of an interrupted
+// call may then stay set, so after arTimeout the communicator must be reset
+// (arCommReset) before further LL calls.  Every workgroup of the grid must be
+// resident at once (the host caps the grid with the occupancy calculator),
+// because consumers wait on producers.
 #include "ar_device.hpp"
 #include "ar_internal.hpp"
 
@@ -42,6 +50,8 @@ constexpr int ll_max_threads(int rmax) { return rmax >= 32 ? 512 : 1024; }
 constexpr int ll_get_batch(int rmax) { return rmax <= 8 ? 2 : 1; }
 // Source words a lane loads before it stores their packets.
 constexpr int kPutBatch = 8;
+// Flag of a ready packet; cleared packet memory reads 0.
+constexpr uint32_t kReady = 1u;
 
 template <typename T, int RMAX, bool EXACT>
 __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX> p)
@@ -51,11 +61,8 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
     const uint32_t nthr = blockDim.x;
     const uint32_t k = blockIdx.x % n;
     const uint32_t b = blockIdx.x / n;
-    uint32_t *ctrl = p.ctrl;
-    __shared__ uint32_t s_flag;
 
-    // put: publish rank k's words of slice b.  The first batch of source
-    // loads is issued before the epoch is read, so the two latencies overlap.
+    // put: publish rank k's words of slice b
     const uint64_t p0 = (uint64_t)b * p.put_per_block;
     const uint64_t p1 = (p0 + p.put_per_block < p.npkt) ? p0 + p.put_per_block : p.npkt;
     const uint32_t *src = (const uint32_t *)p.rk.send[k];
@@ -65,63 +72,31 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
     const uint64_t nfull = p.npkt - p.half_tail;
     const uint64_t pf = p1 < nfull ? p1 : nfull;
     const uint64_t pstep = (uint64_t)kPutBatch * nthr;
-    uint64_t pbase = p0 + threadIdx.x;
-    uint32_t w[kPutBatch];
-#pragma unroll
-    for (int v = 0; v < kPutBatch; ++v) {
-        const uint64_t q = pbase + (uint64_t)v * nthr;
-        if (q < pf)
-            w[v] = src[q];
-    }
-    if (threadIdx.x == 0) {
-        const uint32_t epoch =
-            __hip_atomic_load(ctrl + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_flag = (epoch + 1u == 0u) ? 1u : epoch + 1u;
-    }
-    __syncthreads();
-    const uint32_t flag = s_flag;
-
-    // gfx9 counts loads and stores on one counter that runs out of order
-    // once both are pending, so a load result needed after a store forces a
-    // wait for everything.  One explicit wait here (the loads were in flight
-    // during the epoch read) lets the batch's stores issue back to back.
-    __builtin_amdgcn_s_waitcnt(0);
-
-    for (;;) {
-#pragma unroll
-        for (int v = 0; v < kPutBatch; ++v) {
-            const uint64_t q = pbase + (uint64_t)v * nthr;
-            if (q < pf)
-                put_packet(mine + q, w[v], flag);
-        }
-        pbase += pstep;
-        if (pbase >= pf)
-            break;
+    for (uint64_t pbase = p0 + threadIdx.x; pbase < pf; pbase += pstep) {
+        uint32_t w[kPutBatch];
 #pragma unroll
         for (int v = 0; v < kPutBatch; ++v) {
             const uint64_t q = pbase + (uint64_t)v * nthr;
             if (q < pf)
                 w[v] = src[q];
         }
+        // gfx9 counts loads and stores on one counter that runs out of order
+        // once both are pending, so a load result needed after a store forces
+        // a wait for everything.  One explicit wait for the batch's loads
+        // lets its stores issue back to back.
         __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+        for (int v = 0; v < kPutBatch; ++v) {
+            const uint64_t q = pbase + (uint64_t)v * nthr;
+            if (q < pf)
+                put_packet(mine + q, w[v], kReady);
+        }
     }
     if (p.half_tail && threadIdx.x == 0 && nfull >= p0 && nfull < p1)
-        put_packet(mine + nfull, (uint32_t)((const uint16_t *)(src + nfull))[0], flag);
+        put_packet(mine + nfull, (uint32_t)((const uint16_t *)(src + nfull))[0], kReady);
 
-    // This workgroup holds its copy of the flag, so it can take its ticket;
-    // it does so after its packets are on their way, so that no packet store
-    // waits for the atomic.  The workgroup that takes the last ticket knows
-    // every workgroup has read the epoch and advances it for the next call;
-    // consumers still waiting compare against their own copy.  Relaxed is
-    // enough: the next call reads the epoch only after this kernel has ended.
-    uint32_t ticket = 0;
-    if (threadIdx.x == 0)
-        ticket = __hip_atomic_fetch_add(ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-    // poll, reduce, output: sub-slice k of slice b
-    uint32_t want = flag + p.flag_skew;
-    if (want == 0u)
-        want = 1u;
+    // poll, reduce, clear, output: sub-slice k of slice b
+    const uint32_t want = kReady + p.flag_skew;
     const uint64_t g0 = p0 + (uint64_t)k * p.get_per_block;
     const uint64_t g1 = (g0 + p.get_per_block < p1) ? g0 + p.get_per_block : p1;
     // Two bounds on a lane's total waiting: wall-clock ticks (10 ns each at
@@ -159,7 +134,7 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
             if (wait_start == 0)
                 wait_start = now;
             else if (now - wait_start > p.timeout_ticks || ++spins > spin_limit) {
-                __hip_atomic_store(ctrl + 2, (uint32_t)arTimeout, __ATOMIC_RELAXED,
+                __hip_atomic_store(p.ctrl + 0, (uint32_t)arTimeout, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
                 gave_up = true;
                 break;
@@ -196,6 +171,10 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
                 }
             }
             const uint32_t y = T::narrow(acc);
+#pragma unroll
+            for (int j = 0; j < RMAX; ++j)
+                if (EXACT || j < (int)n)
+                    put_packet(p.pkts + (uint64_t)j * p.pkt_stride + q, 0u, 0u);
             const bool half = p.half_tail && q == p.npkt - 1;
 #pragma unroll
             for (int r = 0; r < RMAX; ++r) {
@@ -209,14 +188,10 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
             }
         }
     }
-
-    if (threadIdx.x == 0 && ticket == gridDim.x - 1) {
-        __hip_atomic_store(ctrl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(ctrl + 0, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
 }
 
-// Clears control words and packets (vector stores; no memset node in graphs).
+// Clears the async-error word and all packets (vector stores; no memset node
+// in graphs).
 __global__ __launch_bounds__(256) void ll_reset(uint64_t *pkts, uint64_t npkts, uint32_t *ctrl)
 {
     const uint64_t i0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -273,11 +248,12 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     p.timeout_ticks = (uint64_t)comm->opt[arOptPollTimeoutUs] * comm->wall_clock_khz / 1000u;
 
     // Default launch shape, measured on MI355X for R = 8 bf16 from 2 KiB to
-    // 1 MiB per rank: 512-thread workgroups (1024 from 1 MiB per rank up),
-    // each publishing about 4096 words, at most 64 workgroups per rank.
+    // 1 MiB per rank: 256-thread workgroups (512 from 512 KiB per rank up),
+    // about two words per lane, at most 64 workgroups per rank (32 from
+    // 256 KiB per rank up).
     int threads = (int)comm->opt[arOptLLThreads];
     if (threads <= 0)
-        threads = p.npkt >= 262144 ? 1024 : 512;
+        threads = p.npkt >= 131072 ? 512 : 256;
     if (threads > ll_max_threads(RMAX))
         threads = ll_max_threads(RMAX);
     const int resident = comm->ll_resident[T::kId][variant_of(nranks)][thread_index(threads)];
@@ -287,9 +263,10 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
 
     uint64_t per_rank = (uint64_t)comm->opt[arOptLLBlocksPerRank];
     if (per_rank == 0) {
-        per_rank = (p.npkt + 4095) / 4096;
-        if (per_rank > 64)
-            per_rank = 64;
+        const uint64_t cap = p.npkt >= 65536 ? 32 : 64;
+        per_rank = (p.npkt + (uint64_t)threads * 2 - 1) / ((uint64_t)threads * 2);
+        if (per_rank > cap)
+            per_rank = cap;
     }
     if (per_rank > max_per_rank)
         per_rank = max_per_rank;

@@ -1,17 +1,19 @@
 #!/usr/bin/env python3
-"""Benchmark of the MI355X sum all-reduce over R = 8 simulated ranks (one GPU).
+"""Benchmark of the MI355X sum all-reduce over R simulated ranks (one GPU).
 
-Prints one JSON line on stdout (a markdown table goes to stderr).
+Prints one JSON line on stdout; a markdown table goes to stderr.
 
-What is timed (inputs resident in HBM before every timed region):
+Default run (inputs resident in HBM before every timed region):
 
 * LL sweep -- R = 8 bf16, 2^k elements per rank for k = 10..19 (2 KiB to
   1 MiB), uniform[-1, 1].  As in the SGLang MSCCL++ benchmark ("SGLang 中的
   MSCCL++ All-Reduce 基准测试与推理集成指南", blog.gitcode.com, section 3.3):
   10 calls captured in one graph, ``--warmup`` untimed replays, then
   ``--steps`` replays inside one HIP event pair; latency per call = elapsed /
-  (steps * 10).  The HB protocol is timed the same way at every size, and LL
-  vs HB at the decode shape 64 x 8192 with N(0, 1) values.
+  (steps * 10).  Each size also gets the guide's eager timing (2 warm-up calls,
+  then the mean of 10 back-to-back calls) for LL and HB, and a timing-only
+  plain-torch row (stack, fp32 sum, cast, copy to every rank).
+* LL vs HB at the decode shape 64 x 8192 with N(0, 1) values.
 * HB prefill -- R = 8 bf16, 8192 x 8192 elements per rank (128 MiB), N(0, 1)
   with 0.1 % of entries x1000, in place.  The roofline figure uses ``--steps``
   launches back to back inside one event pair (the kernel's average launch
@@ -25,6 +27,11 @@ What is timed (inputs resident in HBM before every timed region):
 ``value`` is the mean LL latency per call over the sweep in microseconds
 (lower is better).  Every timed configuration is first checked bit for bit
 against the oracle.
+
+``--configs`` adds every named workload (R = 8 small, the sweep, decode,
+prefill, and R = 16 / 32 with integer data in fp16 and fp32) as rows of one
+table: µs per call, effective GB/s (2 * R * bytes per rank / time), share of
+the 8 TB/s HBM peak, the oracle's time at 1 and at all host threads, parity.
 """
 from __future__ import annotations
 
@@ -39,6 +46,7 @@ METRIC = "all-reduce µs @2KiB–1MiB (R=8, hipGraph) + effective HBM GB/s vs pe
 HBM_PEAK_GBPS = 8000.0
 CALLS_PER_GRAPH = 10
 SWEEP = list(range(10, 20))
+EAGER_WARMUP, EAGER_CALLS = 2, 10
 
 
 def log(msg: str):
@@ -53,9 +61,175 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--only", choices=["all", "sweep", "prefill", "copy"], default="all",
                     help="run one part (for profiler passes)")
+    ap.add_argument("--configs", action="store_true",
+                    help="also measure every named workload and print the full table")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle checks")
     return ap.parse_args()
+
+
+class Bench:
+    """Timing helpers around one communicator; all calls go through arAllReduce."""
+
+    def __init__(self, args):
+        import numpy as np
+        import torch
+
+        import all_reduce_amd as ar
+
+        self.np, self.torch, self.ar, self.args = np, torch, ar, args
+        ar.library()  # fails loudly if the HIP library is not built
+        self.dev = torch.device("cuda", 0)
+        torch.cuda.set_device(self.dev)
+        self.comm = ar.Comm(device=self.dev, max_ranks=32, max_ll_bytes_per_rank=1 << 20)
+        self.codes = {"ll": ar.arProtocol.arProtoLL, "hb": ar.arProtocol.arProtoHB}
+        self.dtypes = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+        self.threads = len(os.sched_getaffinity(0))
+        self.orc = None
+        if not args.no_parity or not args.no_cpu:
+            import oracle
+            self.orc = oracle.load()
+
+    # -- buffers and calls ------------------------------------------------
+    def planes(self, x):
+        R, n = x.shape
+        _, sv = self.ar.rank_buffers(R, n, x.dtype, self.dev)
+        for r in range(R):
+            sv[r].copy_(x[r])
+        _, rv = self.ar.rank_buffers(R, n, x.dtype, self.dev)
+        return sv, rv
+
+    def launch(self, sv, rv, n, proto):
+        dt = self.ar.dtype_code(sv[0].dtype)
+        rc = self.ar.arAllReduce([t.data_ptr() for t in sv], [t.data_ptr() for t in rv], n, dt,
+                                 self.ar.arRedOp.arSum, len(sv), self.codes[proto],
+                                 self.comm.handle, self.torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise self.ar.ArError(rc, "arAllReduce")
+
+    def events(self):
+        E = self.torch.cuda.Event
+        return E(enable_timing=True), E(enable_timing=True)
+
+    # -- parity and the oracle ----------------------------------------------
+    def bits(self, t):
+        t = t.contiguous()
+        if t.dtype == self.torch.float32:
+            return t.cpu().numpy().view(self.np.uint32)
+        return t.view(self.torch.int16).cpu().numpy().view(self.np.uint16)
+
+    def oracle_in(self, x):
+        b = self.bits(x)
+        return b.view(self.np.float32) if x.dtype == self.torch.float32 else b
+
+    def dname(self, t):
+        return {v: k for k, v in self.dtypes.items()}[t.dtype]
+
+    def parity(self, x, rv, sample=None):
+        """Outputs bit-equal to the oracle's (optionally on sampled columns)."""
+        if self.args.no_parity:
+            return None
+        torch, np = self.torch, self.np
+        if sample is not None:
+            x = x[:, sample].contiguous()
+            got = np.stack([self.bits(t[sample.to(t.device)]) for t in rv])
+        else:
+            got = np.stack([self.bits(t) for t in rv])
+        want = self.orc.allreduce(self.oracle_in(x), self.dname(x), nthreads=self.threads)
+        want = want.view(np.uint32) if x.dtype == torch.float32 else want.view(np.uint16)
+        return bool(np.array_equal(got, want))
+
+    def oracle_ms(self, x, nthreads, reps=3):
+        if self.args.no_cpu:
+            return None
+        xi = self.oracle_in(x)
+        out = self.np.empty_like(xi)
+        ts = [self.orc.allreduce_into(list(xi), list(out), self.dname(x), nthreads=nthreads,
+                                      timed=True) for _ in range(reps)]
+        return round(statistics.median(ts) * 1e3, 3)
+
+    # -- timings ------------------------------------------------------------
+    def graph_us(self, sv, rv, n, proto):
+        """µs per call: 10 calls per graph, warmup replays, then steps replays."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                self.launch(sv, rv, n, proto)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(CALLS_PER_GRAPH):
+                self.launch(sv, rv, n, proto)
+        for _ in range(self.args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = self.events()
+        t0.record()
+        for _ in range(self.args.steps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        del g
+        return t0.elapsed_time(t1) * 1000.0 / (self.args.steps * CALLS_PER_GRAPH)
+
+    def eager_us(self, fn):
+        """2 warm-up calls, then the mean of 10 back-to-back calls."""
+        for _ in range(EAGER_WARMUP):
+            fn()
+        self.torch.cuda.synchronize()
+        t0, t1 = self.events()
+        t0.record()
+        for _ in range(EAGER_CALLS):
+            fn()
+        t1.record()
+        self.torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1000.0 / EAGER_CALLS
+
+    def torch_fn(self, sv, rv):
+        """Timing-only plain-torch all-reduce: stack, fp32 sum, cast, copy out."""
+        torch = self.torch
+
+        def fn():
+            y = torch.stack(sv).float().sum(0).to(sv[0].dtype)
+            for t in rv:
+                t.copy_(y)
+        return fn
+
+    def back_to_back_us(self, sv, rv, n, proto, reps):
+        t0, t1 = self.events()
+        t0.record()
+        for _ in range(reps):
+            self.launch(sv, rv, n, proto)
+        t1.record()
+        self.torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1000.0 / reps
+
+    def cold_us(self, plane, backup, sv, rv, n, proto, calls, warmup):
+        """Per-call events; inputs restored and the last-level cache flushed first."""
+        torch = self.torch
+        evict = torch.empty(512 << 20, dtype=torch.uint8, device=self.dev)
+        times = []
+        for i in range(warmup + calls):
+            if backup is not None:
+                plane.copy_(backup)
+            evict.fill_(i & 0xFF)
+            torch.cuda.synchronize()
+            t0, t1 = self.events()
+            t0.record()
+            self.launch(sv, rv, n, proto)
+            t1.record()
+            torch.cuda.synchronize()
+            if i >= warmup:
+                times.append(t0.elapsed_time(t1) * 1000.0)
+        del evict
+        return times
+
+
+def gbps(R, n, esize, us):
+    return round(2 * R * n * esize / (us * 1e-6) / 1e9, 1)
 
 
 def main():
@@ -69,112 +243,54 @@ def main():
         log("bench.py: --steps must be >= 1 and --warmup >= 0")
         return 2
 
-    import numpy as np
     import torch
 
-    import all_reduce_amd as ar
     from all_reduce_amd import inputs
 
     if not torch.cuda.is_available():
         log("bench.py: no GPU visible")
         return 1
-    ar.library()  # fails loudly if the HIP library is not built
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    comm = ar.Comm(device=dev, max_ranks=8, max_ll_bytes_per_rank=1 << 20)
+    B = Bench(args)
     R = 8
-    codes = {"ll": ar.arProtocol.arProtoLL, "hb": ar.arProtocol.arProtoHB}
-
-    def launch(sv, rv, n, proto):
-        rc = ar.arAllReduce([t.data_ptr() for t in sv], [t.data_ptr() for t in rv], n,
-                            ar.arDataType.arBfloat16, ar.arRedOp.arSum, len(sv), codes[proto],
-                            comm.handle, torch.cuda.current_stream().cuda_stream)
-        if rc != 0:
-            raise ar.ArError(rc, "arAllReduce")
-
-    orc = None
-    if not args.no_parity or not args.no_cpu:
-        import oracle
-        orc = oracle.load()
-
-    def bits16(t):
-        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-
-    def parity(x_cpu, rv):
-        if args.no_parity:
-            return None
-        want = orc.allreduce(bits16(x_cpu), "bf16", nthreads=len(os.sched_getaffinity(0)))
-        got = np.stack([bits16(t) for t in rv])
-        return bool(np.array_equal(got, want))
-
-    def graph_time(sv, rv, n, proto):
-        """µs per call: 10 calls per graph, warmup replays, then steps replays."""
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for _ in range(2):
-                launch(sv, rv, n, proto)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(CALLS_PER_GRAPH):
-                launch(sv, rv, n, proto)
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(args.steps):
-            g.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        us = t0.elapsed_time(t1) * 1000.0 / (args.steps * CALLS_PER_GRAPH)
-        del g
-        return us
-
     result = {}
-    rows = []
 
-    # ---- LL sweep (and HB at the same sizes) ------------------------------
+    # ---- LL sweep (HB, eager and plain torch at the same sizes) -------------
     sweep_rows = []
     if args.only in ("all", "sweep"):
         for k in SWEEP:
             case = inputs.sweep(k)
             n = case["count"]
             x = inputs.make(**case)
-            _, sv = ar.rank_buffers(R, n, torch.bfloat16, dev)
-            _, rv = ar.rank_buffers(R, n, torch.bfloat16, dev)
-            for r in range(R):
-                sv[r].copy_(x[r])
+            sv, rv = B.planes(x)
             row = {"bytes_per_rank": 2 * n, "elems_per_rank": n}
             for proto in ("ll", "hb"):
-                launch(sv, rv, n, proto)
+                B.launch(sv, rv, n, proto)
                 torch.cuda.synchronize()
-                row[f"{proto}_parity"] = parity(x, rv)
-                us = graph_time(sv, rv, n, proto)
+                row[f"{proto}_parity"] = B.parity(x, rv)
+                us = B.graph_us(sv, rv, n, proto)
                 row[f"{proto}_us"] = round(us, 3)
-                row[f"{proto}_gbps"] = round(2 * R * 2 * n / (us * 1e-6) / 1e9, 1)
+                row[f"{proto}_gbps"] = gbps(R, n, 2, us)
+                row[f"{proto}_eager_us"] = round(
+                    B.eager_us(lambda: B.launch(sv, rv, n, proto)), 3)
+            row["torch_eager_us"] = round(B.eager_us(B.torch_fn(sv, rv)), 3)
             sweep_rows.append(row)
-            log(f"sweep 2^{k}: LL {row['ll_us']:.2f} us  HB {row['hb_us']:.2f} us")
-        if comm.async_error() != ar.arResult.arSuccess:
+            log(f"sweep 2^{k}: LL {row['ll_us']:.2f} us  HB {row['hb_us']:.2f} us (graph); "
+                f"eager LL {row['ll_eager_us']:.2f} HB {row['hb_eager_us']:.2f} "
+                f"torch {row['torch_eager_us']:.2f}")
+        if B.comm.async_error() != B.ar.arResult.arSuccess:
             raise RuntimeError("LL wait timed out during the sweep")
         result["ll_sweep"] = sweep_rows
 
-        # decode shape, LL vs HB
         case = inputs.WORKLOADS["C3"]
         n = case["count"]
         x = inputs.make(**case)
-        _, sv = ar.rank_buffers(R, n, torch.bfloat16, dev)
-        _, rv = ar.rank_buffers(R, n, torch.bfloat16, dev)
-        for r in range(R):
-            sv[r].copy_(x[r])
+        sv, rv = B.planes(x)
         dec = {"elems_per_rank": n, "tokens": 64, "hidden": 8192}
         for proto in ("ll", "hb"):
-            launch(sv, rv, n, proto)
+            B.launch(sv, rv, n, proto)
             torch.cuda.synchronize()
-            dec[f"{proto}_parity"] = parity(x, rv)
-            dec[f"{proto}_us"] = round(graph_time(sv, rv, n, proto), 3)
+            dec[f"{proto}_parity"] = B.parity(x, rv)
+            dec[f"{proto}_us"] = round(B.graph_us(sv, rv, n, proto), 3)
         result["decode_64x8192"] = dec
         log(f"decode 64x8192: LL {dec['ll_us']:.2f} us  HB {dec['hb_us']:.2f} us")
         del sv, rv
@@ -185,47 +301,30 @@ def main():
         n = case["count"]
         log("prefill: generating 8 x 64M bf16 inputs")
         x = inputs.make(**case)
-        plane, sv = ar.rank_buffers(R, n, torch.bfloat16, dev)
-        backup = torch.empty_like(plane)
+        plane, sv = B.ar.rank_buffers(R, n, torch.bfloat16, B.dev)
         for r in range(R):
             sv[r].copy_(x[r])
-        backup.copy_(plane)
-        evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        launch(sv, sv, n, "hb")
+        backup = plane.clone()
+        B.launch(sv, sv, n, "hb")
         torch.cuda.synchronize()
         pre = {"elems_per_rank": n, "bytes_per_rank": 2 * n, "in_place": True}
-        pre["parity"] = parity(x, sv)
+        pre["parity"] = B.parity(x, sv)
+        if args.configs:
+            pre["oracle_ms_1"] = B.oracle_ms(x, 1, reps=1)
+            pre["oracle_ms_T"] = B.oracle_ms(x, B.threads, reps=1)
         del x
-        times = []
-        for i in range(args.warmup + args.steps):
-            plane.copy_(backup)
-            evict.fill_(i & 0xFF)
-            torch.cuda.synchronize()
-            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            t0.record()
-            launch(sv, sv, n, "hb")
-            t1.record()
-            torch.cuda.synchronize()
-            if i >= args.warmup:
-                times.append(t0.elapsed_time(t1) * 1000.0)
+        times = B.cold_us(plane, backup, sv, sv, n, "hb", args.steps, args.warmup)
         b_alg = 2 * R * 2 * n
         mean_us = statistics.fmean(times)
         pre["us_mean_cold"] = round(mean_us, 2)
         pre["us_median_cold"] = round(statistics.median(times), 2)
         pre["us_min_cold"] = round(min(times), 2)
         # The kernel's average launch duration: steps launches back to back
-        # inside one event pair (each call reads 1 GiB and writes 1 GiB, four
-        # times the last-level cache, so little survives from call to call).
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(args.steps):
-            launch(sv, sv, n, "hb")
-        t1.record()
-        torch.cuda.synchronize()
-        avg_us = t0.elapsed_time(t1) * 1000.0 / args.steps
+        # inside one event pair.
+        avg_us = B.back_to_back_us(sv, sv, n, "hb", args.steps)
         pre["us_per_launch"] = round(avg_us, 2)
-        pre["gbps"] = round(b_alg / (avg_us * 1e-6) / 1e9, 1)
-        pre["gbps_cold"] = round(b_alg / (mean_us * 1e-6) / 1e9, 1)
+        pre["gbps"] = gbps(R, n, 2, avg_us)
+        pre["gbps_cold"] = gbps(R, n, 2, mean_us)
         result["hb_prefill"] = pre
         traffic = _counter_traffic()
         result["roofline"] = {
@@ -238,17 +337,17 @@ def main():
         }
         log(f"prefill HB in place: {pre['us_per_launch']:.1f} us per launch, {pre['gbps']:.0f} GB/s "
             f"({100 * pre['gbps'] / HBM_PEAK_GBPS:.1f}% of 8 TB/s), parity {pre['parity']}")
-        del plane, backup, evict, sv
+        del plane, backup, sv
 
     # ---- plain device copy, for context --------------------------------------
     if args.only in ("all", "copy"):
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=B.dev)
         dst = torch.empty_like(src)
         src.fill_(1)
         for _ in range(args.warmup):
             dst.copy_(src)
         torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0, t1 = B.events()
         t0.record()
         for _ in range(args.steps):
             dst.copy_(src)
@@ -259,19 +358,22 @@ def main():
                                       "gbps": round(2 * (1 << 30) / (us * 1e-6) / 1e9, 1)}
         del src, dst
 
+    # ---- every named workload as one table ----------------------------------
+    if args.configs and args.only == "all":
+        result["configs"] = run_configs(B, inputs, sweep_rows, result)
+
     # ---- oracle on this host's cores -----------------------------------------
     if not args.no_cpu and sweep_rows:
-        cores = len(os.sched_getaffinity(0))
+        cores = B.threads
         per_size = []
         t_start = time.perf_counter()
         for k in SWEEP:
-            case = inputs.sweep(k)
-            xb = bits16(inputs.make(**case))
-            out = np.empty_like(xb)
+            xb = B.oracle_in(inputs.make(**inputs.sweep(k)))
+            out = B.np.empty_like(xb)
             reps, spent = 0, 0.0
             while spent < 1.0 and reps < 2000:
-                spent += orc.allreduce_into(list(xb), list(out), "bf16", nthreads=cores,
-                                            timed=True)
+                spent += B.orc.allreduce_into(list(xb), list(out), "bf16", nthreads=cores,
+                                              timed=True)
                 reps += 1
             per_size.append(spent / reps * 1e6)
         result["cpu_baseline"] = {
@@ -286,11 +388,10 @@ def main():
         }
         log(f"oracle on {cores} threads: mean {result['cpu_baseline']['value']:.1f} us per call")
 
-    if comm.async_error() != ar.arResult.arSuccess:
+    if B.comm.async_error() != B.ar.arResult.arSuccess:
         raise RuntimeError("an LL wait timed out")
-    comm.close()
+    B.comm.close()
 
-    # ---- report ---------------------------------------------------------------
     value = statistics.fmean(r["ll_us"] for r in sweep_rows) if sweep_rows else None
     line = {
         "metric": METRIC,
@@ -318,6 +419,114 @@ def main():
     print(json.dumps(line), flush=True)
     _markdown(line)
     return 0
+
+
+def run_configs(B, inputs, sweep_rows, result):
+    """Rows for every named workload (see the module docstring)."""
+    torch = B.torch
+    T = B.threads
+    rows = []
+
+    def add(name, R, dtype, n, proto, mode, us, parity, o1=None, oT=None):
+        es = 4 if dtype == "fp32" else 2
+        g = gbps(R, n, es, us)
+        rows.append({"config": name, "R": R, "dtype": dtype, "elems_per_rank": n,
+                     "bytes_per_rank": n * es, "proto": proto, "mode": mode,
+                     "us_per_call": round(us, 2), "gbps": g,
+                     "pct_of_peak": round(100 * g / HBM_PEAK_GBPS, 2),
+                     "oracle_ms_1": o1, "oracle_ms_T": oT, "parity": parity})
+
+    # C1: R=8, 1024 bf16, eager calls of each protocol
+    case = inputs.WORKLOADS["C1"]
+    x = inputs.make(**case)
+    sv, rv = B.planes(x)
+    o1, oT = B.oracle_ms(x, 1), B.oracle_ms(x, T)
+    for proto in ("ll", "hb"):
+        B.launch(sv, rv, case["count"], proto)
+        torch.cuda.synchronize()
+        par = B.parity(x, rv)
+        us = B.eager_us(lambda: B.launch(sv, rv, case["count"], proto))
+        add("C1", 8, "bf16", case["count"], proto, "eager", us, par, o1, oT)
+    # C2: the sweep, from the rows already measured
+    for k, r in zip(SWEEP, sweep_rows):
+        x = inputs.make(**inputs.sweep(k))
+        o1, oT = B.oracle_ms(x, 1), B.oracle_ms(x, T)
+        for proto in ("ll", "hb"):
+            add(f"C2 2^{k}", 8, "bf16", r["elems_per_rank"], proto, "graph", r[f"{proto}_us"],
+                r[f"{proto}_parity"], o1, oT)
+            add(f"C2 2^{k}", 8, "bf16", r["elems_per_rank"], proto, "eager",
+                r[f"{proto}_eager_us"], r[f"{proto}_parity"], o1, oT)
+        add(f"C2 2^{k}", 8, "bf16", r["elems_per_rank"], "torch", "eager",
+            r["torch_eager_us"], None, o1, oT)
+    # C3: decode shape
+    d = result.get("decode_64x8192")
+    if d:
+        x = inputs.make(**inputs.WORKLOADS["C3"])
+        o1, oT = B.oracle_ms(x, 1), B.oracle_ms(x, T)
+        for proto in ("ll", "hb"):
+            add("C3 64x8192", 8, "bf16", d["elems_per_rank"], proto, "graph", d[f"{proto}_us"],
+                d[f"{proto}_parity"], o1, oT)
+    # C4: prefill, from the measured rows
+    p = result.get("hb_prefill")
+    if p:
+        add("C4 8192x8192 in place", 8, "bf16", p["elems_per_rank"], "hb", "back-to-back",
+            p["us_per_launch"], p["parity"], p.get("oracle_ms_1"), p.get("oracle_ms_T"))
+        add("C4 8192x8192 in place", 8, "bf16", p["elems_per_rank"], "hb", "cold",
+            p["us_mean_cold"], p["parity"], p.get("oracle_ms_1"), p.get("oracle_ms_T"))
+    # C5a: R = 16 / 32, 2^18 fp16 integers, both protocols, graph-timed
+    for R in (16, 32):
+        case = inputs.integer_case(R, "fp16")
+        x = inputs.make(**case)
+        n = case["count"]
+        sv, rv = B.planes(x)
+        o1, oT = B.oracle_ms(x, 1), B.oracle_ms(x, T)
+        for proto in ("ll", "hb"):
+            B.launch(sv, rv, n, proto)
+            torch.cuda.synchronize()
+            par = B.parity(x, rv)
+            exact = torch.equal(rv[0].cpu().to(torch.int64), x.to(torch.int64).sum(0))
+            add(f"C5a R={R}", R, "fp16", n, proto, "graph", B.graph_us(sv, rv, n, proto),
+                None if par is None else (par and exact), o1, oT)
+        del sv, rv
+        log(f"C5a R={R} done")
+    # C5b: R = 16 / 32, 4096 x 7168 fp32 integers, HB out of place
+    for R in (16, 32):
+        case = inputs.integer_case(R, "fp32")
+        log(f"C5b R={R}: generating {R} x {case['count']} fp32 inputs")
+        x = inputs.make(**case)
+        n = case["count"]
+        sv, rv = B.planes(x)
+        B.launch(sv, rv, n, "hb")
+        torch.cuda.synchronize()
+        g = torch.Generator().manual_seed(99)
+        sample = torch.randint(0, n, (1 << 20,), generator=g)
+        par = B.parity(x, rv, sample=sample)
+        exact = True
+        step = 1 << 22
+        for a in range(0, n, step):
+            want = x[:, a:a + step].to(torch.int32).sum(0)
+            exact &= torch.equal(rv[R - 1][a:a + step].cpu().to(torch.int32), want)
+        o1 = B.oracle_ms(x, 1, reps=1)
+        oT = B.oracle_ms(x, T, reps=1)
+        us_b2b = B.back_to_back_us(sv, rv, n, "hb", B.args.steps)
+        us_cold = statistics.fmean(B.cold_us(None, None, sv, rv, n, "hb", B.args.steps,
+                                             B.args.warmup))
+        ok = None if par is None else (par and exact)
+        add(f"C5b R={R}", R, "fp32", n, "hb", "back-to-back", us_b2b, ok, o1, oT)
+        add(f"C5b R={R}", R, "fp32", n, "hb", "cold", us_cold, ok, o1, oT)
+        del x, sv, rv
+        log(f"C5b R={R} done")
+
+    log("\n| config | R | dtype | elems/rank | bytes/rank | proto | mode | µs/call | eff. GB/s | "
+        "% of 8 TB/s | oracle ms (1 thr) | oracle ms (T thr) | parity |")
+    log("|---|---:|---|---:|---:|---|---|---:|---:|---:|---:|---:|:---:|")
+    for r in rows:
+        log(f"| {r['config']} | {r['R']} | {r['dtype']} | {r['elems_per_rank']} | "
+            f"{r['bytes_per_rank']} | {r['proto']} | {r['mode']} | {r['us_per_call']:.2f} | "
+            f"{r['gbps']:.0f} | {r['pct_of_peak']:.1f} | {r['oracle_ms_1']} | {r['oracle_ms_T']} | "
+            f"{r['parity']} |")
+    log(f"(T = {T} host threads)")
+    return rows
 
 
 def _sources_digest() -> str:
@@ -364,11 +573,13 @@ def _cpu_model() -> str:
 def _markdown(line: dict):
     rows = line.get("ll_sweep", [])
     if rows:
-        log("\n| bytes/rank | LL µs | LL GB/s | HB µs | HB GB/s | parity |")
-        log("|---:|---:|---:|---:|---:|:---:|")
+        log("\n| bytes/rank | LL graph µs | HB graph µs | LL eager µs | HB eager µs | "
+            "torch eager µs | LL GB/s | HB GB/s | parity LL/HB |")
+        log("|---:|---:|---:|---:|---:|---:|---:|---:|:---:|")
         for r in rows:
-            log(f"| {r['bytes_per_rank']} | {r['ll_us']:.2f} | {r['ll_gbps']:.0f} | "
-                f"{r['hb_us']:.2f} | {r['hb_gbps']:.0f} | {r['ll_parity']}/{r['hb_parity']} |")
+            log(f"| {r['bytes_per_rank']} | {r['ll_us']:.2f} | {r['hb_us']:.2f} | "
+                f"{r['ll_eager_us']:.2f} | {r['hb_eager_us']:.2f} | {r['torch_eager_us']:.2f} | "
+                f"{r['ll_gbps']:.0f} | {r['hb_gbps']:.0f} | {r['ll_parity']}/{r['hb_parity']} |")
 
 
 if __name__ == "__main__":

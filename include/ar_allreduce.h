@@ -94,7 +94,7 @@ typedef enum {
      * above 16 ranks); 0 = default. */
     arOptLLThreads = 6,
     /* HB: threads per workgroup (64 .. 1024, a multiple of 64; capped at 512
-     * above 8 ranks and 256 above 16); 0 = default (256). */
+     * above 8 ranks and 256 above 16); 0 = default (256, or 128 from 32 ranks). */
     arOptHBThreads = 7,
     /* HB: which elements simulated rank c reduces (its chunk) -- 0: the
      * contiguous c-th of R equal parts, 1: every R-th tile starting at tile c
@@ -106,11 +106,11 @@ typedef enum {
 /* Create a communicator on `device` for groups of up to `maxRanks` (1..32)
  * simulated ranks and LL messages of up to `maxLLBytesPerRank` bytes per rank.
  * It owns device memory for the LL packets (2 * maxRanks * maxLLBytesPerRank
- * bytes, each 4-byte payload travels in an 8-byte packet) and a few control
- * words (the packet epoch, a workgroup ticket, the asynchronous error).
- * maxLLBytesPerRank may be 0 (HB only).  Allocates with hipMalloc, so it must
- * not be called while a stream is being captured.  The caller's current
- * device is left unchanged.
+ * bytes, each 4-byte payload travels in an 8-byte packet; all zero between
+ * calls) and a word that records an asynchronous error.  maxLLBytesPerRank
+ * may be 0 (HB only).  Allocates with hipMalloc, so it must not be called
+ * while a stream is being captured.  The caller's current device is left
+ * unchanged.
  * Returns arInvalidArgument for a NULL `comm` or out-of-range sizes,
  * arHipError if the device or memory is not available. */
 arResult_t arCommCreate(arComm_t *comm, int device, int maxRanks, size_t maxLLBytesPerRank);
@@ -118,9 +118,11 @@ arResult_t arCommCreate(arComm_t *comm, int device, int maxRanks, size_t maxLLBy
 /* Free the communicator.  Work that uses it must have finished. */
 arResult_t arCommDestroy(arComm_t comm);
 
-/* Enqueue, on `stream`, a kernel that clears the LL packets, the epoch and the
+/* Enqueue, on `stream`, a kernel that clears the LL packets and the
  * asynchronous error, so that the communicator can be used again after a
- * timeout.  No allocation and no memset node: safe to capture in a graph. */
+ * timeout (an LL call that timed out may leave packets set; LL results are
+ * undefined until the reset).  No allocation and no memset node: safe to
+ * capture in a graph. */
 arResult_t arCommReset(arComm_t comm, arStream_t stream);
 
 /* Read the asynchronous error recorded by earlier kernels: arSuccess or
