@@ -42,6 +42,7 @@ class arRedOp(IntEnum):
 class arProtocol(IntEnum):
     arProtoLL = 0
     arProtoHB = 1
+    arProtoAuto = 2
 
 
 class arOption(IntEnum):
@@ -85,6 +86,9 @@ def library() -> ctypes.CDLL:
         "arCommSetOption": ([vp, i32, i64], i32),
         "arCommGetOption": ([vp, i32, ctypes.POINTER(i64)], i32),
         "arAllReduce": ([ctypes.POINTER(vp), ctypes.POINTER(vp), sz, i32, i32, i32, i32, vp, vp], i32),
+        "arCommTune": ([vp, i32, i32, sz, vp], i32),
+        "arCommGetTunedShape": ([vp, i32, i32, i32, sz, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                 ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float)], i32),
         "arGetErrorString": ([i32], ctypes.c_char_p),
         "arGetVersion": ([], i32),
     }
@@ -137,6 +141,19 @@ def arCommGetOption(comm, option: int):
     return r, v.value
 
 
+def arCommTune(comm, dtype: int, nranks: int, max_bytes_per_rank: int, stream) -> int:
+    return library().arCommTune(comm, int(dtype), nranks, max_bytes_per_rank, stream)
+
+
+def arCommGetTunedShape(comm, dtype: int, nranks: int, protocol: int, bytes_per_rank: int):
+    """Returns (result code, tuned, threads, blocks, microseconds)."""
+    v, t, b, u = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_float(0.0)
+    r = library().arCommGetTunedShape(comm, int(dtype), nranks, int(protocol), bytes_per_rank,
+                                      ctypes.byref(v), ctypes.byref(t), ctypes.byref(b),
+                                      ctypes.byref(u))
+    return r, v.value, t.value, b.value, u.value
+
+
 def arAllReduce(sendbufs: Sequence[int] | None, recvbufs: Sequence[int] | None, count: int,
                 dtype: int, op: int, nranks: int, protocol: int, comm, stream) -> int:
     """Device pointers as integers; ``None`` passes a NULL array."""
@@ -164,7 +181,8 @@ def dtype_code(dtype) -> arDataType:
 
 def protocol_code(protocol) -> arProtocol:
     if isinstance(protocol, str):
-        return {"ll": arProtocol.arProtoLL, "hb": arProtocol.arProtoHB}[protocol.lower()]
+        return {"ll": arProtocol.arProtoLL, "hb": arProtocol.arProtoHB,
+                "auto": arProtocol.arProtoAuto}[protocol.lower()]
     return arProtocol(protocol)
 
 
@@ -232,6 +250,22 @@ class Comm:
         if r != 0:
             raise ArError(r, "arCommGetOption")
         return v
+
+    def tune(self, dtype, nranks: int, max_bytes_per_rank: int, stream=None):
+        """Measure launch shapes per power-of-two size (see arCommTune)."""
+        r = arCommTune(self.handle, dtype_code(dtype), nranks, max_bytes_per_rank,
+                       self._stream(stream))
+        if r != 0:
+            raise ArError(r, "arCommTune")
+
+    def tuned_shape(self, dtype, nranks: int, protocol, bytes_per_rank: int):
+        """(threads, blocks, us) stored for that size -- (0, 0, us) when the
+        built-in default won -- or None if never tuned."""
+        r, v, t, b, u = arCommGetTunedShape(self.handle, dtype_code(dtype), nranks,
+                                            protocol_code(protocol), bytes_per_rank)
+        if r != 0:
+            raise ArError(r, "arCommGetTunedShape")
+        return None if v == 0 else (t, b, u)
 
     def reset(self, stream=None):
         r = arCommReset(self.handle, self._stream(stream))

@@ -18,6 +18,7 @@
 #include <string.h>
 
 #include <new>
+#include <vector>
 
 #include "ar_internal.hpp"
 
@@ -71,7 +72,7 @@ arResult_t validate(const void *const *sendbufs, void *const *recvbufs, size_t c
         return reject(arUnsupported, "only arSum is implemented");
     if (nranks < 1 || nranks > AR_MAX_RANKS)
         return reject(arUnsupported, "nranks must be in 1..32");
-    if (protocol != arProtoLL && protocol != arProtoHB)
+    if (protocol != arProtoLL && protocol != arProtoHB && protocol != arProtoAuto)
         return reject(arInvalidArgument, "unknown protocol");
     if (count == 0)
         return arSuccess;
@@ -105,6 +106,43 @@ arResult_t validate(const void *const *sendbufs, void *const *recvbufs, size_t c
         }
     }
     return arSuccess;
+}
+
+// Size bucket of a message: ceil(log2(bytes per rank)).
+int bucket_of(size_t bytes)
+{
+    int b = 0;
+    while (b < ar::kBuckets - 1 && ((size_t)1 << b) < bytes)
+        ++b;
+    return b;
+}
+
+bool ll_possible(const arComm *comm, int nranks, size_t bytes)
+{
+    return nranks <= comm->max_ranks && bytes <= comm->max_ll_bytes;
+}
+
+// The protocol a call runs: arProtoAuto resolves to the tuned faster one.
+arProtocol_t resolve_protocol(const arComm *comm, arDataType_t dtype, int nranks, size_t bytes,
+                              arProtocol_t protocol)
+{
+    if (protocol != arProtoAuto)
+        return protocol;
+    const int b = bucket_of(bytes);
+    const ar::TunedShape &ll = comm->tuned[dtype][nranks][arProtoLL][b];
+    const ar::TunedShape &hb = comm->tuned[dtype][nranks][arProtoHB][b];
+    if (ll_possible(comm, nranks, bytes) && ll.valid && (!hb.valid || ll.us < hb.us))
+        return arProtoLL;
+    return arProtoHB;
+}
+
+hipError_t launch(const void *const *send, void *const *recv, size_t count, arDataType_t dtype,
+                  int nranks, arProtocol_t proto, const arComm *comm, int threads,
+                  uint64_t blocks, hipStream_t stream)
+{
+    return proto == arProtoLL
+               ? ar::launch_ll(send, recv, count, (int)dtype, nranks, comm, threads, blocks, stream)
+               : ar::launch_hb(send, recv, count, (int)dtype, nranks, comm, threads, blocks, stream);
 }
 
 // RAII restore of the caller's current device.
@@ -290,22 +328,163 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
         return r;
     if (comm == nullptr)
         return reject(arInvalidArgument, "NULL comm");
-    if (protocol == arProtoLL) {
+    const size_t bytes = count * elem_bytes(dtype);
+    const arProtocol_t proto = resolve_protocol(comm, dtype, nranks, bytes, protocol);
+    if (proto == arProtoLL) {
         if (nranks > comm->max_ranks)
             return reject(arInvalidUsage, "nranks above the communicator's maxRanks");
-        if (count * elem_bytes(dtype) > comm->max_ll_bytes)
+        if (bytes > comm->max_ll_bytes)
             return reject(arInvalidUsage, "message above the communicator's maxLLBytesPerRank");
     }
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess || cur != comm->device)
         return reject(arInvalidUsage, "the communicator's device is not the current device");
 
-    const hipError_t e =
-        protocol == arProtoLL
-            ? ar::launch_ll(sendbufs, recvbufs, count, (int)dtype, nranks, comm, (hipStream_t)stream)
-            : ar::launch_hb(sendbufs, recvbufs, count, (int)dtype, nranks, comm, (hipStream_t)stream);
+    // Launch shape: explicit options, else the tuned shape of this size, else
+    // the built-in defaults (0).
+    int threads = (int)comm->opt[proto == arProtoLL ? arOptLLThreads : arOptHBThreads];
+    uint64_t blocks = (uint64_t)comm->opt[proto == arProtoLL ? arOptLLBlocksPerRank : arOptHBBlocks];
+    if (threads == 0 && blocks == 0) {
+        const ar::TunedShape &t = comm->tuned[dtype][nranks][proto][bucket_of(bytes)];
+        if (t.valid) {
+            threads = t.threads;
+            blocks = (uint64_t)t.blocks;
+        }
+    }
+    const hipError_t e = launch(sendbufs, recvbufs, count, dtype, nranks, proto, comm, threads,
+                                blocks, (hipStream_t)stream);
     if (e != hipSuccess)
         return reject(arHipError, hipGetErrorString(e));
+    return arSuccess;
+}
+
+arResult_t arCommTune(arComm_t comm, arDataType_t dtype, int nranks, size_t maxBytesPerRank,
+                      arStream_t stream)
+{
+    if (comm == nullptr)
+        return reject(arInvalidArgument, "NULL comm");
+    if (dtype != arBfloat16 && dtype != arFloat16 && dtype != arFloat32)
+        return reject(arUnsupported, "dtype must be bf16, fp16 or fp32");
+    if (nranks < 1 || nranks > AR_MAX_RANKS)
+        return reject(arUnsupported, "nranks must be in 1..32");
+    if (maxBytesPerRank < 512 || maxBytesPerRank > ((size_t)1 << 34))
+        return reject(arInvalidArgument, "maxBytesPerRank must be in 512 B .. 16 GiB");
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != comm->device)
+        return reject(arInvalidUsage, "the communicator's device is not the current device");
+
+    const size_t es = elem_bytes(dtype);
+    const size_t stride = (maxBytesPerRank + 255) / 256 * 256;
+    char *splane = nullptr, *rplane = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    const hipStream_t st = (hipStream_t)stream;
+    arResult_t result = arSuccess;
+    if (hipMalloc((void **)&splane, stride * (size_t)nranks) != hipSuccess ||
+        hipMalloc((void **)&rplane, stride * (size_t)nranks) != hipSuccess ||
+        hipMemset(splane, 0x3c, stride * (size_t)nranks) != hipSuccess ||
+        hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        result = reject(arHipError, "tuning set-up failed");
+    }
+    std::vector<const void *> send((size_t)nranks);
+    std::vector<void *> recv((size_t)nranks);
+    for (int r = 0; r < nranks && result == arSuccess; ++r) {
+        send[(size_t)r] = splane + (size_t)r * stride;
+        recv[(size_t)r] = rplane + (size_t)r * stride;
+    }
+
+    // Candidate shapes: the built-in default first, then the (threads per
+    // workgroup, workgroups) grid it was chosen from.  The launchers clamp each
+    // to what the kernel and the message allow.  A candidate replaces the best
+    // so far only if it is more than 3 % faster, so timing noise does not move
+    // the choice away from the default.
+    static const int kLLThreads[] = {256, 512, 1024};
+    static const int kLLBlocks[] = {1, 2, 4, 8, 16, 32, 64};
+    static const int kHBThreads[] = {128, 256, 512};
+    const int hb_blocks[] = {comm->cu_count / 2, comm->cu_count, comm->cu_count * 2};
+
+    const int top = bucket_of(maxBytesPerRank);
+    for (int b = 9; b <= top && result == arSuccess; ++b) {
+        size_t bytes = ((size_t)1 << b) < maxBytesPerRank ? ((size_t)1 << b) : maxBytesPerRank;
+        const size_t count = bytes / es > 0 ? bytes / es : 1;
+        bytes = count * es;
+        // about 200 us of timed work per candidate, between 5 and 20 calls
+        const double est_us = (double)(2 * (size_t)nranks * bytes) / 5.0e3 + 3.0;
+        int calls = (int)(200.0 / est_us);
+        calls = calls < 5 ? 5 : (calls > 20 ? 20 : calls);
+        for (int proto = arProtoLL; proto <= arProtoHB && result == arSuccess; ++proto) {
+            if (proto == arProtoLL && !ll_possible(comm, nranks, bytes))
+                continue;
+            const int nb = proto == arProtoLL ? 7 : 3;
+            ar::TunedShape best = {0, 0, 0, 0.0f};
+            for (int c = -1; c < 3 * nb && result == arSuccess; ++c) {
+                const int th = c < 0 ? 0 : (proto == arProtoLL ? kLLThreads[c / nb] : kHBThreads[c / nb]);
+                const int bl = c < 0 ? 0 : (proto == arProtoLL ? kLLBlocks[c % nb] : hb_blocks[c % nb]);
+                float us = 0.0f;
+                hipError_t e = hipSuccess;
+                for (int i = 0; i < 2 && e == hipSuccess; ++i)
+                    e = launch(send.data(), recv.data(), count, dtype, nranks,
+                               (arProtocol_t)proto, comm, th, (uint64_t)bl, st);
+                for (int rep = 0; rep < 2 && e == hipSuccess; ++rep) {
+                    e = hipEventRecord(e0, st);
+                    for (int i = 0; i < calls && e == hipSuccess; ++i)
+                        e = launch(send.data(), recv.data(), count, dtype, nranks,
+                                   (arProtocol_t)proto, comm, th, (uint64_t)bl, st);
+                    if (e == hipSuccess)
+                        e = hipEventRecord(e1, st);
+                    if (e == hipSuccess)
+                        e = hipEventSynchronize(e1);
+                    float ms = 0.0f;
+                    if (e == hipSuccess)
+                        e = hipEventElapsedTime(&ms, e0, e1);
+                    const float t = ms * 1000.0f / (float)calls;
+                    if (rep == 0 || t < us)
+                        us = t;
+                }
+                if (e != hipSuccess) {
+                    result = reject(arHipError, hipGetErrorString(e));
+                    break;
+                }
+                if (!best.valid || us < 0.97f * best.us)
+                    best = {1, th, bl, us};
+            }
+            if (result == arSuccess)
+                comm->tuned[dtype][nranks][proto][b] = best;
+        }
+    }
+    if (e0 != nullptr)
+        (void)hipEventDestroy(e0);
+    if (e1 != nullptr)
+        (void)hipEventDestroy(e1);
+    if (hipDeviceSynchronize() != hipSuccess && result == arSuccess)
+        result = reject(arHipError, "synchronisation after tuning failed");
+    (void)hipFree(splane);
+    (void)hipFree(rplane);
+    if (result == arSuccess) {
+        uint32_t word = 0;
+        if (hipMemcpy(&word, comm->ctrl + 0, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+            result = reject(arHipError, "reading the error word failed");
+        else if (word != 0)
+            result = reject(arTimeout, "an LL wait timed out while tuning");
+    }
+    return result;
+}
+
+arResult_t arCommGetTunedShape(arComm_t comm, arDataType_t dtype, int nranks,
+                               arProtocol_t protocol, size_t bytesPerRank, int *tuned,
+                               int *threads, int *blocks, float *us)
+{
+    if (comm == nullptr || tuned == nullptr || threads == nullptr || blocks == nullptr ||
+        us == nullptr)
+        return reject(arInvalidArgument, "NULL argument");
+    if ((dtype != arBfloat16 && dtype != arFloat16 && dtype != arFloat32) || nranks < 1 ||
+        nranks > AR_MAX_RANKS || (protocol != arProtoLL && protocol != arProtoHB) ||
+        bytesPerRank == 0)
+        return reject(arInvalidArgument, "argument out of range");
+    const ar::TunedShape &t = comm->tuned[dtype][nranks][protocol][bucket_of(bytesPerRank)];
+    *tuned = t.valid;
+    *threads = t.threads;
+    *blocks = t.blocks;
+    *us = t.us;
     return arSuccess;
 }
 

@@ -60,6 +60,20 @@ constexpr int kThreadChoices = 5; // 64, 128, 256, 512, 1024
 
 constexpr int kOptionCount = 9;
 
+namespace ar {
+// One tuned launch shape: threads per workgroup and workgroups (HB: the
+// whole grid; LL: per simulated rank), with the time it measured.  0 threads
+// and 0 blocks mean the built-in default shape won.  valid == 0: not tuned.
+struct TunedShape {
+    int32_t valid;
+    int32_t threads;
+    int32_t blocks;
+    float us;
+};
+// Message sizes are bucketed by ceil(log2(bytes per rank)).
+constexpr int kBuckets = 41;
+}  // namespace ar
+
 struct arComm {
     int device;
     int max_ranks;
@@ -71,16 +85,23 @@ struct arComm {
     uint32_t *ctrl;        // control words; [0] is the async error
     int64_t opt[kOptionCount]; // indexed by arOption_t
     int ll_resident[3][ar::kRankVariants + 1][ar::kThreadChoices];
+    // [dtype][nranks][protocol][bucket]; filled by arCommTune
+    ar::TunedShape tuned[3][AR_MAX_RANKS + 1][2][ar::kBuckets];
 };
 
 namespace ar {
 
 // Launchers: validate nothing (the ABI layer did), pick the instantiation,
-// enqueue on `stream`.  Return hipSuccess or the launch error.
+// enqueue on `stream`.  `threads` and `blocks` give the launch shape (HB: the
+// whole grid; LL: workgroups per rank); 0 picks the built-in default.  Both
+// are clamped to what the kernel and the message allow.  Return hipSuccess or
+// the launch error.
 hipError_t launch_hb(const void *const *send, void *const *recv, size_t count, int dtype,
-                     int nranks, const arComm *comm, hipStream_t stream);
+                     int nranks, const arComm *comm, int threads, uint64_t blocks,
+                     hipStream_t stream);
 hipError_t launch_ll(const void *const *send, void *const *recv, size_t count, int dtype,
-                     int nranks, const arComm *comm, hipStream_t stream);
+                     int nranks, const arComm *comm, int threads, uint64_t blocks,
+                     hipStream_t stream);
 hipError_t launch_reset(const arComm *comm, hipStream_t stream);
 // Fills comm->ll_resident from the occupancy calculator.
 hipError_t query_ll_residency(arComm *comm);

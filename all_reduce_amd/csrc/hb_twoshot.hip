@@ -164,7 +164,8 @@ hipError_t launch_unroll(const HBParams<RMAX> &p, uint32_t grid, uint32_t thread
 
 template <typename T, int RMAX, bool EXACT>
 hipError_t launch_table(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, hipStream_t stream)
+                        const arComm *comm, int want_threads, uint64_t want_blocks,
+                        hipStream_t stream)
 {
     constexpr uint64_t kPerVec = 16 / T::kBytes;
     HBParams<RMAX> p = {};
@@ -184,12 +185,10 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     const bool nt = comm->opt[arOptHBNonTemporal] != 0;
     // Default: 256 threads (128 from 32 ranks up), one workgroup per CU --
     // measured on MI355X, fewer loads in flight per CU stream HBM faster.
-    uint32_t threads = comm->opt[arOptHBThreads] > 0 ? (uint32_t)comm->opt[arOptHBThreads]
-                                                     : (nranks >= 32 ? 128u : 256u);
+    uint32_t threads = want_threads > 0 ? (uint32_t)want_threads : (nranks >= 32 ? 128u : 256u);
     if (threads > (uint32_t)hb_max_threads(RMAX))
         threads = (uint32_t)hb_max_threads(RMAX);
-    const uint64_t blocks = comm->opt[arOptHBBlocks] > 0 ? (uint64_t)comm->opt[arOptHBBlocks]
-                                                         : (uint64_t)comm->cu_count;
+    const uint64_t blocks = want_blocks > 0 ? want_blocks : (uint64_t)comm->cu_count;
 
     // Enough workgroups to fill the chip, but never more per chunk than the
     // largest chunk has tiles.
@@ -209,35 +208,36 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
 
 template <typename T>
 hipError_t launch_dtype(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, hipStream_t stream)
+                        const arComm *comm, int th, uint64_t bl, hipStream_t stream)
 {
     switch (nranks) {
-    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, comm, stream);
-    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, comm, stream);
-    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, comm, stream);
-    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, comm, stream);
-    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, comm, stream);
-    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, comm, stream);
+    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, comm, th, bl, stream);
+    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, comm, th, bl, stream);
+    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, comm, th, bl, stream);
+    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, comm, th, bl, stream);
+    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, comm, th, bl, stream);
+    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, comm, th, bl, stream);
     default: break;
     }
     if (nranks < 4)
-        return launch_table<T, 4, false>(send, recv, count, nranks, comm, stream);
+        return launch_table<T, 4, false>(send, recv, count, nranks, comm, th, bl, stream);
     if (nranks < 8)
-        return launch_table<T, 8, false>(send, recv, count, nranks, comm, stream);
+        return launch_table<T, 8, false>(send, recv, count, nranks, comm, th, bl, stream);
     if (nranks < 16)
-        return launch_table<T, 16, false>(send, recv, count, nranks, comm, stream);
-    return launch_table<T, 32, false>(send, recv, count, nranks, comm, stream);
+        return launch_table<T, 16, false>(send, recv, count, nranks, comm, th, bl, stream);
+    return launch_table<T, 32, false>(send, recv, count, nranks, comm, th, bl, stream);
 }
 
 }  // namespace
 
 hipError_t launch_hb(const void *const *send, void *const *recv, size_t count, int dtype,
-                     int nranks, const arComm *comm, hipStream_t stream)
+                     int nranks, const arComm *comm, int threads, uint64_t blocks,
+                     hipStream_t stream)
 {
     switch (dtype) {
-    case kBf16: return launch_dtype<Bf16>(send, recv, count, nranks, comm, stream);
-    case kFp16: return launch_dtype<Fp16>(send, recv, count, nranks, comm, stream);
-    default: return launch_dtype<Fp32>(send, recv, count, nranks, comm, stream);
+    case kBf16: return launch_dtype<Bf16>(send, recv, count, nranks, comm, threads, blocks, stream);
+    case kFp16: return launch_dtype<Fp16>(send, recv, count, nranks, comm, threads, blocks, stream);
+    default: return launch_dtype<Fp32>(send, recv, count, nranks, comm, threads, blocks, stream);
     }
 }
 

@@ -230,7 +230,8 @@ int variant_of(int nranks)
 
 template <typename T, int RMAX, bool EXACT>
 hipError_t launch_table(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, hipStream_t stream)
+                        const arComm *comm, int want_threads, uint64_t want_blocks,
+                        hipStream_t stream)
 {
     LLParams<RMAX> p = {};
     for (int r = 0; r < nranks; ++r) {
@@ -251,7 +252,7 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     // 1 MiB per rank: 256-thread workgroups (512 from 512 KiB per rank up),
     // about two words per lane, at most 64 workgroups per rank (32 from
     // 256 KiB per rank up).
-    int threads = (int)comm->opt[arOptLLThreads];
+    int threads = want_threads;
     if (threads <= 0)
         threads = p.npkt >= 131072 ? 512 : 256;
     if (threads > ll_max_threads(RMAX))
@@ -261,7 +262,7 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     if (max_per_rank < 1)
         max_per_rank = 1;
 
-    uint64_t per_rank = (uint64_t)comm->opt[arOptLLBlocksPerRank];
+    uint64_t per_rank = want_blocks;
     if (per_rank == 0) {
         const uint64_t cap = p.npkt >= 65536 ? 32 : 64;
         per_rank = (p.npkt + (uint64_t)threads * 2 - 1) / ((uint64_t)threads * 2);
@@ -285,16 +286,16 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
 
 template <typename T>
 hipError_t launch_dtype(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, hipStream_t stream)
+                        const arComm *comm, int th, uint64_t bl, hipStream_t stream)
 {
     switch (nranks) {
-    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, comm, stream);
-    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, comm, stream);
-    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, comm, stream);
-    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, comm, stream);
-    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, comm, stream);
-    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, comm, stream);
-    default: return launch_table<T, 32, false>(send, recv, count, nranks, comm, stream);
+    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, comm, th, bl, stream);
+    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, comm, th, bl, stream);
+    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, comm, th, bl, stream);
+    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, comm, th, bl, stream);
+    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, comm, th, bl, stream);
+    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, comm, th, bl, stream);
+    default: return launch_table<T, 32, false>(send, recv, count, nranks, comm, th, bl, stream);
     }
 }
 
@@ -333,12 +334,13 @@ hipError_t query_dtype(int (*tab)[kThreadChoices])
 }  // namespace
 
 hipError_t launch_ll(const void *const *send, void *const *recv, size_t count, int dtype,
-                     int nranks, const arComm *comm, hipStream_t stream)
+                     int nranks, const arComm *comm, int threads, uint64_t blocks,
+                     hipStream_t stream)
 {
     switch (dtype) {
-    case kBf16: return launch_dtype<Bf16>(send, recv, count, nranks, comm, stream);
-    case kFp16: return launch_dtype<Fp16>(send, recv, count, nranks, comm, stream);
-    default: return launch_dtype<Fp32>(send, recv, count, nranks, comm, stream);
+    case kBf16: return launch_dtype<Bf16>(send, recv, count, nranks, comm, threads, blocks, stream);
+    case kFp16: return launch_dtype<Fp16>(send, recv, count, nranks, comm, threads, blocks, stream);
+    default: return launch_dtype<Fp32>(send, recv, count, nranks, comm, threads, blocks, stream);
     }
 }
 

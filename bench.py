@@ -5,6 +5,9 @@ Prints one JSON line on stdout; a markdown table goes to stderr.
 
 Default run (inputs resident in HBM before every timed region):
 
+* start-up tuning -- arCommTune for bf16, R = 8, every power-of-two size up to
+  128 MiB per rank (the guide's section 4.4: each size timed over launch-shape
+  candidates, the fastest kept); ``--no-tune`` uses the built-in shapes.
 * LL sweep -- R = 8 bf16, 2^k elements per rank for k = 10..19 (2 KiB to
   1 MiB), uniform[-1, 1].  As in the SGLang MSCCL++ benchmark ("SGLang 中的
   MSCCL++ All-Reduce 基准测试与推理集成指南", blog.gitcode.com, section 3.3):
@@ -63,6 +66,8 @@ def parse():
                     help="run one part (for profiler passes)")
     ap.add_argument("--configs", action="store_true",
                     help="also measure every named workload and print the full table")
+    ap.add_argument("--no-tune", action="store_true",
+                    help="skip the start-up tuning (arCommTune); use the built-in launch shapes")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle checks")
     return ap.parse_args()
@@ -254,6 +259,23 @@ def main():
     R = 8
     result = {}
 
+    # Start-up tuning, as SGLang's MSCCL++ integration does (guide section
+    # 4.4): every power-of-two size of the bf16 R = 8 workloads, both protocols.
+    if not args.no_tune and args.only in ("all", "sweep", "prefill"):
+        t0 = time.perf_counter()
+        B.comm.tune(torch.bfloat16, R, 128 << 20)
+        result["tuning"] = {"dtype": "bf16", "nranks": R, "max_bytes_per_rank": 128 << 20,
+                            "wall_s": round(time.perf_counter() - t0, 2)}
+        log(f"arCommTune bf16 R=8 up to 128 MiB per rank: {result['tuning']['wall_s']} s")
+
+    # Untimed warm-up of both protocols and the graph path at the first size.
+    if args.only in ("all", "sweep"):
+        xw = inputs.make(**inputs.sweep(SWEEP[0]))
+        sv, rv = B.planes(xw)
+        for proto in ("ll", "hb"):
+            B.graph_us(sv, rv, xw.shape[1], proto)
+        del sv, rv
+
     # ---- LL sweep (HB, eager and plain torch at the same sizes) -------------
     sweep_rows = []
     if args.only in ("all", "sweep"):
@@ -273,6 +295,10 @@ def main():
                 row[f"{proto}_eager_us"] = round(
                     B.eager_us(lambda: B.launch(sv, rv, n, proto)), 3)
             row["torch_eager_us"] = round(B.eager_us(B.torch_fn(sv, rv)), 3)
+            for proto in ("ll", "hb"):
+                shape = B.comm.tuned_shape(torch.bfloat16, R, proto, 2 * n)
+                row[f"{proto}_shape"] = (("default" if shape[0] == 0 else list(shape[:2]))
+                                         if shape else None)
             sweep_rows.append(row)
             log(f"sweep 2^{k}: LL {row['ll_us']:.2f} us  HB {row['hb_us']:.2f} us (graph); "
                 f"eager LL {row['ll_eager_us']:.2f} HB {row['hb_eager_us']:.2f} "
@@ -413,6 +439,7 @@ def main():
                          "at 8192x8192 per rank (128 MiB) for the HBM roofline"),
             "nranks": R, "calls_per_graph": CALLS_PER_GRAPH,
             "parallelism": "1 GPU, ranks simulated in HBM",
+            "tuned": not args.no_tune,
         },
     }
     line.update(result)

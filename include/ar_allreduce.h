@@ -67,7 +67,9 @@ typedef enum { arBfloat16 = 0, arFloat16 = 1, arFloat32 = 2 } arDataType_t;
 
 typedef enum { arSum = 0 } arRedOp_t;
 
-typedef enum { arProtoLL = 0, arProtoHB = 1 } arProtocol_t;
+/* arProtoAuto picks, per message size, the protocol that arCommTune measured
+ * faster (HB where nothing was tuned). */
+typedef enum { arProtoLL = 0, arProtoHB = 1, arProtoAuto = 2 } arProtocol_t;
 
 /* Tunables and test hooks, see arCommSetOption.  The launch-shape options
  * are the (workgroups, threads per workgroup) pairs that an auto-tuner would
@@ -135,6 +137,43 @@ arResult_t arCommGetAsyncError(arComm_t comm, arResult_t *asyncError);
 arResult_t arCommSetOption(arComm_t comm, arOption_t option, int64_t value);
 arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
 
+/* Measure launch shapes and keep the fastest, per message size -- the
+ * start-up tuning of SGLang's MSCCL++ integration ("SGLang 中的 MSCCL++
+ * All-Reduce 基准测试与推理集成指南", blog.gitcode.com, section 4.4: every
+ * power-of-two size timed over (workgroups, threads per workgroup) candidates,
+ * the best kept for the life of the process).
+ *
+ * For `dtype` and `nranks`, every power-of-two size from 512 bytes up to
+ * maxBytesPerRank per rank (the last bucket at maxBytesPerRank itself) is
+ * timed with each protocol the communicator can run at that size, over the
+ * built-in default shape and a fixed set of candidates; a candidate wins only
+ * if it is more than 3 % faster than the best before it, and the winner and
+ * its time are stored in the communicator.  Later calls of that dtype and rank count use the stored
+ * shape of their size bucket (the message size rounded up to a power of two)
+ * unless arOptLLThreads/arOptLLBlocksPerRank (LL) or arOptHBThreads/
+ * arOptHBBlocks (HB) are set; arProtoAuto then picks the faster protocol.
+ * Tuning again overwrites the table; sizes never tuned use built-in defaults.
+ *
+ * Allocates two scratch planes of nranks * maxBytesPerRank bytes for the
+ * duration, runs on `stream` and synchronises the device: never call it while
+ * a stream is being captured.  Returns arInvalidArgument for a NULL comm or
+ * maxBytesPerRank outside 512 B .. 16 GiB, arUnsupported for a dtype or rank
+ * count arAllReduce would reject, arInvalidUsage if the communicator is not on
+ * the current device, arHipError if memory or a launch fails, arTimeout if an
+ * LL wait ran out during tuning (then reset the communicator). */
+arResult_t arCommTune(arComm_t comm, arDataType_t dtype, int nranks, size_t maxBytesPerRank,
+                      arStream_t stream);
+
+/* The tuned shape for (dtype, nranks, protocol LL or HB) at a message of
+ * bytesPerRank bytes.  *tuned = 0 when that size was never tuned.  Otherwise
+ * *threads and *blocks are the threads per workgroup and workgroups (HB: the
+ * grid; LL: per rank) that won -- both 0 when the built-in default shape won --
+ * and *us the time per call measured for it, in microseconds.  Returns
+ * arInvalidArgument for NULL pointers or out-of-range arguments. */
+arResult_t arCommGetTunedShape(arComm_t comm, arDataType_t dtype, int nranks,
+                               arProtocol_t protocol, size_t bytesPerRank, int *tuned,
+                               int *threads, int *blocks, float *us);
+
 /* The sum all-reduce.
  *
  *  sendbufs  host array of `nranks` device pointers; sendbufs[r] holds rank
@@ -147,7 +186,7 @@ arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
  *  dtype     arBfloat16, arFloat16 or arFloat32 (else arUnsupported).
  *  op        arSum only (else arUnsupported).
  *  nranks    1..32 (else arUnsupported); 1 is a copy.
- *  protocol  arProtoLL or arProtoHB (else arInvalidArgument).
+ *  protocol  arProtoLL, arProtoHB or arProtoAuto (else arInvalidArgument).
  *  comm      a communicator on the current device.
  *  stream    the stream to enqueue on.
  *
@@ -156,7 +195,8 @@ arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
  * receive buffer may coincide exactly with the same rank's send buffer, and
  * send buffers may overlap one another (they are only read).
  * LL also needs nranks <= the communicator's maxRanks and count * element
- * size <= its maxLLBytesPerRank (arInvalidUsage otherwise).
+ * size <= its maxLLBytesPerRank (arInvalidUsage otherwise); arProtoAuto only
+ * picks LL where it can run.
  *
  * The call only enqueues work and returns; the buffers belong to the caller
  * and must stay valid until the work has run (for a captured graph, as long

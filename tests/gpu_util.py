@@ -12,7 +12,8 @@ import pins
 
 CODES = {"bf16": ar.arDataType.arBfloat16, "fp16": ar.arDataType.arFloat16,
          "fp32": ar.arDataType.arFloat32}
-PROTO = {"ll": ar.arProtocol.arProtoLL, "hb": ar.arProtocol.arProtoHB}
+PROTO = {"ll": ar.arProtocol.arProtoLL, "hb": ar.arProtocol.arProtoHB,
+         "auto": ar.arProtocol.arProtoAuto}
 TORCH = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
 
 

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     lib = ar.library()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
@@ -57,7 +57,7 @@ CASES = [
     ("bad op", dict(op=1), "arUnsupported", "arSum"),
     ("zero ranks", dict(nranks=0), "arUnsupported", "nranks"),
     ("33 ranks", dict(nranks=33), "arUnsupported", "nranks"),
-    ("bad protocol", dict(protocol=2), "arInvalidArgument", "protocol"),
+    ("bad protocol", dict(protocol=3), "arInvalidArgument", "protocol"),
     ("NULL send array", dict(send=None), "arInvalidArgument", "NULL buffer array"),
     ("NULL recv array", dict(recv=None), "arInvalidArgument", "NULL buffer array"),
     ("NULL rank pointer", dict(send=[A, 0]), "arInvalidArgument", "NULL rank buffer"),
@@ -129,6 +129,8 @@ def test_comm_arguments_checked_before_the_device():
     assert ar.arCommSetOption(None, 0, 1) == ar.arResult.arInvalidArgument
     assert ar.arCommGetOption(None, 0)[0] == ar.arResult.arInvalidArgument
     assert ar.arCommGetAsyncError(None)[0] == ar.arResult.arInvalidArgument
+    assert ar.arCommTune(None, 0, 8, 1 << 20, None) == ar.arResult.arInvalidArgument
+    assert ar.arCommGetTunedShape(None, 0, 8, 0, 1024)[0] == ar.arResult.arInvalidArgument
 
 
 def test_comm_create_without_a_gpu_reports_hip_error():
@@ -143,6 +145,7 @@ def test_python_helpers():
     import torch
     assert ar.protocol_code("LL") == ar.arProtocol.arProtoLL
     assert ar.protocol_code("hb") == ar.arProtocol.arProtoHB
+    assert ar.protocol_code("auto") == ar.arProtocol.arProtoAuto
     assert ar.dtype_code(torch.bfloat16) == ar.arDataType.arBfloat16
     assert ar.dtype_code(torch.float32) == ar.arDataType.arFloat32
     with pytest.raises(ar.ArError):

@@ -1,0 +1,73 @@
+"""Size-bucketed tuning (arCommTune) and arProtoAuto, on the GPU.
+
+Tuning only changes launch shapes, so every result must stay bit-exact with
+the oracle; the tuned table must cover every power-of-two size it was asked
+for, for each protocol the communicator can run there.
+"""
+import pytest
+import torch
+
+import all_reduce_amd as ar
+from all_reduce_amd import inputs
+from gpu_util import assert_parity, expect, note, run_allreduce
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def comm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    c = ar.Comm(device="cuda:0", max_ranks=16, max_ll_bytes_per_rank=1 << 20)
+    note("arCommTune bf16 R=8 up to 4 MiB, fp32 R=16 up to 256 KiB")
+    c.tune(torch.bfloat16, 8, 4 << 20)
+    c.tune(torch.float32, 16, 256 << 10)
+    yield c
+    c.close()
+
+
+def test_table_covers_the_tuned_sizes(comm):
+    for b in range(9, 23):
+        hb = comm.tuned_shape(torch.bfloat16, 8, "hb", 1 << b)
+        assert hb is not None and hb[0] in (0, 128, 256, 512) and hb[2] > 0
+        ll = comm.tuned_shape(torch.bfloat16, 8, "ll", 1 << b)
+        if (1 << b) <= comm.max_ll_bytes_per_rank:
+            assert ll is not None and ll[0] in (0, 256, 512, 1024) and ll[2] > 0
+        else:
+            assert ll is None, "LL cannot run above maxLLBytesPerRank"
+    # sizes round up to their bucket; untuned dtype / rank counts stay untuned
+    assert comm.tuned_shape(torch.bfloat16, 8, "hb", 3000) == comm.tuned_shape(
+        torch.bfloat16, 8, "hb", 4096)
+    assert comm.tuned_shape(torch.float16, 8, "hb", 4096) is None
+    assert comm.tuned_shape(torch.bfloat16, 8, "hb", 1 << 23) is None
+    assert comm.tuned_shape(torch.float32, 16, "ll", 1 << 18) is not None
+
+
+@pytest.mark.parametrize("protocol", ["ll", "hb", "auto"])
+@pytest.mark.parametrize("k", [10, 13, 16, 19, 21])
+def test_tuned_shapes_keep_bits(comm, orc, protocol, k):
+    if protocol == "ll" and ((1 << k) + 3) * 2 > comm.max_ll_bytes_per_rank:
+        pytest.skip("above the communicator's LL limit")
+    x = inputs.make(8, (1 << k) + 3, "bf16", "outliers", seed=60 + k)
+    assert_parity(run_allreduce(comm, x, protocol), expect(orc, x), f"tuned {protocol} 2^{k}")
+
+
+def test_auto_on_untuned_sizes_and_fp32(comm, orc):
+    x = inputs.make(16, 50_001, "fp32", "normal", seed=70)
+    assert_parity(run_allreduce(comm, x, "auto"), expect(orc, x), "auto fp32 R=16")
+    y = inputs.make(3, 10_007, "fp16", "normal", seed=71)
+    assert_parity(run_allreduce(comm, y, "auto"), expect(orc, y), "auto fp16 R=3 untuned")
+    assert comm.async_error() == ar.arResult.arSuccess
+
+
+def test_options_override_the_table(comm, orc):
+    x = inputs.make(8, 1 << 16, "bf16", "normal", seed=72)
+    want = expect(orc, x)
+    try:
+        comm.set_option(ar.arOption.arOptLLThreads, 64)
+        comm.set_option(ar.arOption.arOptHBThreads, 64)
+        for proto in ("ll", "hb", "auto"):
+            assert_parity(run_allreduce(comm, x, proto), want, f"override {proto}")
+    finally:
+        comm.set_option(ar.arOption.arOptLLThreads, 0)
+        comm.set_option(ar.arOption.arOptHBThreads, 0)
