@@ -63,6 +63,9 @@ class Oracle:
             fn = getattr(lib, name)
             fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
             fn.restype = None
+        lib.oracle_allreduce_grouped.argtypes = [vpp, vpp, ctypes.c_size_t, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.oracle_allreduce_grouped.restype = ctypes.c_int
         lib.oracle_widen_fp16_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_size_t]
         lib.oracle_widen_fp16_array.restype = None
@@ -115,6 +118,22 @@ class Oracle:
         if self.lib.oracle_allreduce(sp, rp, count, code, len(send), nthreads) != 0:
             raise RuntimeError("oracle_allreduce failed")
         return None
+
+    def allreduce_grouped(self, x: np.ndarray, dtype: str, group: int,
+                          nthreads: int = 1) -> np.ndarray:
+        """Hierarchical order: groups of ``group`` consecutive ranks summed first
+        (binary32), then the group partials in group order; one rounding."""
+        x = np.ascontiguousarray(x)
+        out = np.empty_like(x)
+        code = DTYPES[dtype]
+        want = np.float32 if code == FP32 else np.uint16
+        if x.dtype != want:
+            raise ValueError(f"oracle: dtype {np.dtype(want)} expected")
+        sp, rp = self._ptrs(list(x)), self._ptrs(list(out))
+        if self.lib.oracle_allreduce_grouped(sp, rp, x.shape[1], code, x.shape[0], group,
+                                             nthreads) != 0:
+            raise ValueError("oracle_allreduce_grouped: bad arguments")
+        return out
 
     def allreduce(self, x: np.ndarray, dtype: str, nthreads: int = 1) -> np.ndarray:
         """``x`` has shape (R, N); returns a new (R, N) array of outputs."""

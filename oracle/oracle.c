@@ -195,6 +195,62 @@ int oracle_allreduce(const void *const *send, void *const *recv, size_t count,
     return 0;
 }
 
+/* Hierarchical (two-level) order: ranks form nranks / group consecutive
+ * groups ("nodes") of `group` ranks.  For every element, each group's partial
+ * sum is taken in binary32 in rank order within the group, starting from the
+ * group's first rank; the partials are then summed in binary32 in group
+ * order, starting from group 0's; the result is rounded once (RNE).  This is
+ * the order of an all-reduce that reduces inside each node first and across
+ * nodes second ("SGLang 中的 MSCCL++ All-Reduce 基准测试与推理集成指南",
+ * blog.gitcode.com, section 4.4: multi-node algorithms for TP = 16 / 32),
+ * with the cross-node partials kept in binary32.  group == nranks (and
+ * group == 1) is the flat order of oracle_allreduce.
+ * Returns 0, or -1 on an unknown dtype, nranks < 1, group < 1 or a group that
+ * does not divide nranks. */
+static float grouped_sum(const void *const *send, ptrdiff_t i, int dtype, int nranks, int group)
+{
+    float total = 0.0f;
+    for (int g = 0; g < nranks / group; ++g) {
+        float part = 0.0f;
+        for (int l = 0; l < group; ++l) {
+            const int j = g * group + l;
+            float x;
+            if (dtype == ORACLE_BF16)
+                x = oracle_widen_bf16(((const uint16_t *)send[j])[i]);
+            else if (dtype == ORACLE_FP16)
+                x = oracle_widen_fp16(((const uint16_t *)send[j])[i]);
+            else
+                x = ((const float *)send[j])[i];
+            part = (l == 0) ? x : part + x;
+        }
+        total = (g == 0) ? part : total + part;
+    }
+    return total;
+}
+
+int oracle_allreduce_grouped(const void *const *send, void *const *recv, size_t count,
+                             int dtype, int nranks, int group, int nthreads)
+{
+    if (nranks < 1 || group < 1 || nranks % group != 0 || dtype < ORACLE_BF16 ||
+        dtype > ORACLE_FP32)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (ptrdiff_t i = 0; i < (ptrdiff_t)count; ++i) {
+        const float a = grouped_sum(send, i, dtype, nranks, group);
+        for (int r = 0; r < nranks; ++r) {
+            if (dtype == ORACLE_BF16)
+                ((uint16_t *)recv[r])[i] = oracle_rne_bf16(a);
+            else if (dtype == ORACLE_FP16)
+                ((uint16_t *)recv[r])[i] = oracle_rne_fp16(a);
+            else
+                ((float *)recv[r])[i] = a;
+        }
+    }
+    return 0;
+}
+
 /* Array forms of the converters, for the exhaustive converter pins. */
 void oracle_rne_bf16_array(const float *in, uint16_t *out, size_t n, int nthreads)
 {

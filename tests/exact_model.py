@@ -172,3 +172,17 @@ def value_of(bits: int, dtype: str):
 
 def is_nan_bits(bits: int, dtype: str) -> bool:
     return decode(bits, FORMATS[dtype])[0] == "nan"
+
+
+def allreduce_column_grouped(bits: list[int], dtype: str, group: int) -> int:
+    """Hierarchical order: binary32 partial per group of ``group`` consecutive
+    ranks (in rank order), then the partials summed in group order; one final
+    rounding to the format."""
+    fmt = FORMATS[dtype]
+    total = None
+    for g in range(len(bits) // group):
+        part = decode(bits[g * group], fmt)
+        for b in bits[g * group + 1:(g + 1) * group]:
+            part = add_exact_then_round(part, decode(b, fmt), FP32)
+        total = part if total is None else add_exact_then_round(total, part, FP32)
+    return encode(round_to(total, fmt), fmt)

@@ -380,3 +380,73 @@ def pin_widen_fp16(orc):
     got = orc.widen_fp16(h)
     want = h.view(np.float16).astype(np.float32)
     assert_same_bits(got, want.view(np.uint32), "fp32", "widen_fp16 vs numpy")
+
+
+# ---------------------------------------------------------------------------
+# hierarchical (grouped) order
+# ---------------------------------------------------------------------------
+GOLDEN_GROUPED = Path(__file__).resolve().parent / "golden" / "hand_cases_grouped.txt"
+
+
+def pin_grouped_hand_cases(orc):
+    n = 0
+    for line in GOLDEN_GROUPED.read_text().splitlines():
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        dtype, group, ins, out = [t.strip() for t in line.split("|")]
+        cols = [[int(t, 16) for t in ins.split()]]
+        got = orc.allreduce_grouped(to_array(cols, dtype), dtype, int(group))
+        for r in range(len(cols[0])):
+            assert_same_bits(got[r], np.array([int(out, 16)]), dtype,
+                             f"grouped hand case {dtype} g={group} {ins}")
+        n += 1
+    assert n >= 5, "grouped hand-case fixture went missing"
+
+
+@functools.lru_cache(maxsize=None)
+def _grouped_cols(dtype: str, R: int, group: int, ncols: int, seed: int):
+    rng = np.random.default_rng(seed)
+    bits = random_bits(rng, dtype, (ncols, R))
+    want = np.array([em.allreduce_column_grouped([int(b) for b in row], dtype, group)
+                     for row in bits], dtype=np.int64)
+    return bits, want
+
+
+def pin_grouped_random(orc, dtype: str, R: int, group: int, ncols: int, seed: int = 3):
+    bits, want = _grouped_cols(dtype, R, group, ncols, seed)
+    x = bits.T.copy()
+    if dtype == "fp32":
+        x = x.view(np.float32)
+    out = orc.allreduce_grouped(x, dtype, group, nthreads=2)
+    for r in range(R):
+        assert_same_bits(out[r], want, dtype, f"grouped {dtype} R={R} g={group} rank {r}")
+
+
+@functools.lru_cache(maxsize=None)
+def _grouped_exhaustive(dtype: str):
+    vals = VALUE_SETS[dtype][:16]
+    cols = [list(c) for c in itertools.product(vals, repeat=4)]
+    want = np.array([em.allreduce_column_grouped(c, dtype, 2) for c in cols], dtype=np.int64)
+    return cols, want
+
+
+def pin_grouped_exhaustive(orc, dtype: str):
+    """Every 4-rank column over 16 values, groups of 2, against the exact model."""
+    cols, want = _grouped_exhaustive(dtype)
+    out = orc.allreduce_grouped(to_array(cols, dtype), dtype, 2, nthreads=2)
+    for r in range(4):
+        assert_same_bits(out[r], want, dtype, f"grouped exhaustive {dtype} rank {r}")
+
+
+def pin_grouped_integer(orc, dtype: str, R: int, group: int, n: int = 4096, seed: int = 9):
+    rng = np.random.default_rng(seed + R)
+    ints = rng.integers(-4, 5, (R, n), dtype=np.int64)
+    fmt = em.FORMATS[dtype]
+    enc = {v: em.encode(("fin", 1 if v < 0 else 0, Fraction(abs(v))), fmt) for v in range(-4, 5)}
+    x = np.vectorize(enc.get)(ints).astype(np.uint32 if dtype == "fp32" else np.uint16)
+    if dtype == "fp32":
+        x = x.view(np.float32)
+    out = orc.allreduce_grouped(x, dtype, group)
+    assert_same_bits(out[0], _exact_int_bits(ints.sum(axis=0), dtype), dtype,
+                     f"grouped integer {dtype} R={R} g={group}")

@@ -59,6 +59,13 @@ MUTANTS = {
     "fp16 widening exponent": ("mag = ldexpf((float)(m | 0x400u), (int)e - 25);",
                                "mag = ldexpf((float)(m | 0x400u), (int)e - 24);"),
     "fp16 subnormal widening": ("mag = ldexpf((float)m, -24);", "mag = ldexpf((float)m, -25);"),
+    # the hierarchical order
+    "grouped partial from +0": ("            part = (l == 0) ? x : part + x;",
+                                "            part = (l == 0) ? 0.0f + x : part + x;"),
+    "grouped sums groups in reverse": ("    for (int g = 0; g < nranks / group; ++g) {",
+                                       "    for (int g = nranks / group - 1; g >= 0; --g) {"),
+    "grouped drops the last group": ("    for (int g = 0; g < nranks / group; ++g) {",
+                                     "    for (int g = 0; g < nranks / group - 1; ++g) {"),
 }
 
 
@@ -72,6 +79,10 @@ def quick_battery(orc):
         pins.pin_invariants(orc, dtype)
     pins.pin_converters(orc, pins.converter_patterns_sample(n=1 << 18))
     pins.pin_widen_fp16(orc)
+    pins.pin_grouped_hand_cases(orc)
+    for dtype in ("bf16", "fp32"):
+        pins.pin_grouped_random(orc, dtype, 16, 8, 1500)
+    pins.pin_grouped_exhaustive(orc, "fp32")
 
 
 def _build_variant(tmp_path: Path, text: str) -> "oracle.Oracle":

@@ -90,3 +90,41 @@ def test_in_place_equals_out_of_place(orc):
     y = x.copy()
     orc.allreduce_into(list(y), list(y), "bf16")
     assert np.array_equal(y, want)
+
+
+# ---- the hierarchical (grouped) order ----------------------------------------
+def test_grouped_hand_cases(orc):
+    pins.pin_grouped_hand_cases(orc)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_grouped_exhaustive_R4_groups_of_2(orc, dtype):
+    pins.pin_grouped_exhaustive(orc, dtype)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("R,group,ncols", [(16, 8, 1500), (32, 8, 800), (8, 2, 2000), (8, 4, 2000)])
+def test_grouped_random(orc, dtype, R, group, ncols):
+    pins.pin_grouped_random(orc, dtype, R, group, ncols)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("R,group", [(16, 8), (32, 8), (32, 4)])
+def test_grouped_integer_closed_form(orc, dtype, R, group):
+    pins.pin_grouped_integer(orc, dtype, R, group)
+
+
+def test_grouped_rejects_bad_groups(orc):
+    x = np.zeros((6, 4), dtype=np.uint16)
+    for g in (0, 4, 7):
+        with pytest.raises(ValueError):
+            orc.allreduce_grouped(x, "bf16", g)
+
+
+def test_grouped_orders_really_differ(orc):
+    # the pins above would pass for the flat order too if the two never differed
+    rng = np.random.default_rng(12)
+    x = pins.random_bits(rng, "fp32", (16, 20000), emin=-20, emax=20).view(np.float32)
+    flat = orc.allreduce(x, "fp32")
+    grouped = orc.allreduce_grouped(x, "fp32", 8)
+    assert int((flat[0].view(np.uint32) != grouped[0].view(np.uint32)).sum()) > 100
