@@ -55,6 +55,7 @@ class arOption(IntEnum):
     arOptLLThreads = 6
     arOptHBThreads = 7
     arOptHBChunkLayout = 8
+    arOptHBGroup = 9
 
 
 AR_MAX_RANKS = 32

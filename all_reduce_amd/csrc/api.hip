@@ -60,6 +60,7 @@ constexpr int64_t kDefaults[kOptionCount] = {
     0,        // arOptLLThreads (auto)
     0,        // arOptHBThreads (auto)
     1,        // arOptHBChunkLayout (interleaved tiles)
+    0,        // arOptHBGroup (flat order)
 };
 
 // Argument checks shared by every protocol.  No HIP call.
@@ -138,11 +139,19 @@ arProtocol_t resolve_protocol(const arComm *comm, arDataType_t dtype, int nranks
 
 hipError_t launch(const void *const *send, void *const *recv, size_t count, arDataType_t dtype,
                   int nranks, arProtocol_t proto, const arComm *comm, int threads,
-                  uint64_t blocks, hipStream_t stream)
+                  uint64_t blocks, int group, hipStream_t stream)
 {
     return proto == arProtoLL
                ? ar::launch_ll(send, recv, count, (int)dtype, nranks, comm, threads, blocks, stream)
-               : ar::launch_hb(send, recv, count, (int)dtype, nranks, comm, threads, blocks, stream);
+               : ar::launch_hb(send, recv, count, (int)dtype, nranks, comm, threads, blocks, group,
+                               stream);
+}
+
+// Ranks per simulated node when a hierarchical order is in force, else 0.
+int hierarchy_group(const arComm *comm, int nranks)
+{
+    const int g = (int)comm->opt[arOptHBGroup];
+    return g > 1 && g < nranks ? g : 0;
 }
 
 // RAII restore of the caller's current device.
@@ -301,6 +310,7 @@ arResult_t arCommSetOption(arComm_t comm, arOption_t option, int64_t value)
         break;
     case arOptHBThreads: ok = value >= 0 && value <= 1024 && value % 64 == 0; break;
     case arOptHBChunkLayout: ok = value == 0 || value == 1; break;
+    case arOptHBGroup: ok = value >= 0 && value <= AR_MAX_RANKS; break;
     default: return reject(arInvalidArgument, "unknown option");
     }
     if (!ok)
@@ -329,7 +339,13 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
     if (comm == nullptr)
         return reject(arInvalidArgument, "NULL comm");
     const size_t bytes = count * elem_bytes(dtype);
-    const arProtocol_t proto = resolve_protocol(comm, dtype, nranks, bytes, protocol);
+    const int group = hierarchy_group(comm, nranks);
+    if (group != 0 && nranks % group != 0)
+        return reject(arInvalidUsage, "nranks is not a multiple of arOptHBGroup");
+    if (group != 0 && protocol == arProtoLL)
+        return reject(arUnsupported, "LL sums in the flat order only (arOptHBGroup is set)");
+    const arProtocol_t proto =
+        group != 0 ? arProtoHB : resolve_protocol(comm, dtype, nranks, bytes, protocol);
     if (proto == arProtoLL) {
         if (nranks > comm->max_ranks)
             return reject(arInvalidUsage, "nranks above the communicator's maxRanks");
@@ -352,7 +368,7 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
         }
     }
     const hipError_t e = launch(sendbufs, recvbufs, count, dtype, nranks, proto, comm, threads,
-                                blocks, (hipStream_t)stream);
+                                blocks, group, (hipStream_t)stream);
     if (e != hipSuccess)
         return reject(arHipError, hipGetErrorString(e));
     return arSuccess;
@@ -423,12 +439,12 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype, int nranks, size_t maxB
                 hipError_t e = hipSuccess;
                 for (int i = 0; i < 2 && e == hipSuccess; ++i)
                     e = launch(send.data(), recv.data(), count, dtype, nranks,
-                               (arProtocol_t)proto, comm, th, (uint64_t)bl, st);
+                               (arProtocol_t)proto, comm, th, (uint64_t)bl, 0, st);
                 for (int rep = 0; rep < 2 && e == hipSuccess; ++rep) {
                     e = hipEventRecord(e0, st);
                     for (int i = 0; i < calls && e == hipSuccess; ++i)
                         e = launch(send.data(), recv.data(), count, dtype, nranks,
-                                   (arProtocol_t)proto, comm, th, (uint64_t)bl, st);
+                                   (arProtocol_t)proto, comm, th, (uint64_t)bl, 0, st);
                     if (e == hipSuccess)
                         e = hipEventRecord(e1, st);
                     if (e == hipSuccess)

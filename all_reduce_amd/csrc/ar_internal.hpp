@@ -29,6 +29,8 @@ struct HBParams {
     uint32_t nranks;      // runtime rank count (the generic kernel; else == R)
     uint32_t tail_elems;  // elements after the last whole vector
     uint32_t interleaved; // 0: chunk c = contiguous vectors; 1: tiles c, c+R, c+2R, ...
+    uint32_t group;       // hierarchical order: ranks per node (1 < group < nranks); else 0
+    uint32_t pad;
 };
 
 // One-shot LL launch parameters.
@@ -58,7 +60,7 @@ constexpr int kThreadChoices = 5; // 64, 128, 256, 512, 1024
 
 }  // namespace ar
 
-constexpr int kOptionCount = 9;
+constexpr int kOptionCount = 10;
 
 namespace ar {
 // One tuned launch shape: threads per workgroup and workgroups (HB: the
@@ -96,8 +98,11 @@ namespace ar {
 // whole grid; LL: workgroups per rank); 0 picks the built-in default.  Both
 // are clamped to what the kernel and the message allow.  Return hipSuccess or
 // the launch error.
+// `group` > 0 selects the hierarchical summation order (groups of `group`
+// consecutive ranks first, then the group partials); the caller guarantees
+// 1 < group < nranks and nranks % group == 0.
 hipError_t launch_hb(const void *const *send, void *const *recv, size_t count, int dtype,
-                     int nranks, const arComm *comm, int threads, uint64_t blocks,
+                     int nranks, const arComm *comm, int threads, uint64_t blocks, int group,
                      hipStream_t stream);
 hipError_t launch_ll(const void *const *send, void *const *recv, size_t count, int dtype,
                      int nranks, const arComm *comm, int threads, uint64_t blocks,

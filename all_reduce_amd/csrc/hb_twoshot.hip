@@ -57,11 +57,20 @@ constexpr int hb_max_threads(int rmax) { return rmax >= 32 ? 256 : (rmax >= 16 ?
 // RMAX: size of the rank table.  EXACT: nranks == RMAX at compile time;
 // otherwise nranks < RMAX arrives at run time and ranks >= nranks are skipped.
 // U: 16-byte vectors per lane per rank in flight.  NT: non-temporal access.
+// NODE: summation order.  0 is the flat order 0..R-1.  Otherwise the
+// hierarchical order: the ranks form nodes of consecutive ranks, each node's
+// partial is summed in binary32 in rank order, then the partials in node
+// order, then one rounding (what an all-reduce that reduces inside each node
+// first and across nodes second computes, with binary32 cross-node partials).
+// NODE > 0 fixes the node size at compile time, so that every fold below is
+// placed by the compiler; NODE < 0 takes it from p.group at run time.
 // The workgroup size is a launch parameter (a tile is blockDim.x * U vectors).
-template <typename T, int RMAX, bool EXACT, int U, bool NT>
+template <typename T, int RMAX, bool EXACT, int U, bool NT, int NODE>
 __global__ __launch_bounds__(hb_max_threads(RMAX)) void hb_twoshot(HBParams<RMAX> p)
 {
+    constexpr bool kGrouped = NODE != 0;
     const uint32_t n = EXACT ? RMAX : p.nranks;
+    const uint32_t node = NODE > 0 ? (uint32_t)NODE : p.group;
     const uint32_t nthr = blockDim.x;
     const uint32_t c = blockIdx.x % n;       // chunk, and the simulated rank owning it
     const uint32_t bb = blockIdx.x / n;      // this workgroup's place among the chunk's
@@ -101,16 +110,31 @@ __global__ __launch_bounds__(hb_max_threads(RMAX)) void hb_twoshot(HBParams<RMAX
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     float acc[T::kPerWord];
+                    float total[T::kPerWord] = {};
                     T::widen(v[u][0][q], acc);
 #pragma unroll
                     for (int j = 1; j < RMAX; ++j) {
                         if (EXACT || j < (int)n) {
                             float x[T::kPerWord];
                             T::widen(v[u][j][q], x);
+                            if (kGrouped && j % node == 0) {
+                                // a node is complete: fold its partial in
 #pragma unroll
-                            for (int e = 0; e < T::kPerWord; ++e)
-                                acc[e] = acc[e] + x[e];
+                                for (int e = 0; e < T::kPerWord; ++e) {
+                                    total[e] = j == node ? acc[e] : total[e] + acc[e];
+                                    acc[e] = x[e];
+                                }
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < T::kPerWord; ++e)
+                                    acc[e] = acc[e] + x[e];
+                            }
                         }
+                    }
+                    if (kGrouped) {
+#pragma unroll
+                        for (int e = 0; e < T::kPerWord; ++e)
+                            acc[e] = total[e] + acc[e];
                     }
                     y[q] = T::narrow(acc);
                 }
@@ -127,8 +151,18 @@ __global__ __launch_bounds__(hb_max_threads(RMAX)) void hb_twoshot(HBParams<RMAX
         constexpr uint64_t kPerVec = 16 / T::kBytes;
         const uint64_t i = p.nvec * kPerVec + threadIdx.x;
         float a = load_elem<T>(p.rk.send[0], i);
-        for (uint32_t j = 1; j < n; ++j)
-            a = a + load_elem<T>(p.rk.send[j], i);
+        float total = 0.0f;
+        for (uint32_t j = 1; j < n; ++j) {
+            const float x = load_elem<T>(p.rk.send[j], i);
+            if (kGrouped && j % node == 0) {
+                total = j == node ? a : total + a;
+                a = x;
+            } else {
+                a = a + x;
+            }
+        }
+        if (kGrouped)
+            a = total + a;
         for (uint32_t r = 0; r < n; ++r)
             store_elem<T>(p.rk.recv[r], i, a);
     }
@@ -136,11 +170,36 @@ __global__ __launch_bounds__(hb_max_threads(RMAX)) void hb_twoshot(HBParams<RMAX
 
 namespace {
 
-template <typename T, int RMAX, bool EXACT, int U, bool NT>
+template <typename T, int RMAX, bool EXACT, int U, bool NT, int NODE = 0>
 hipError_t launch_one(const HBParams<RMAX> &p, uint32_t grid, uint32_t threads, hipStream_t stream)
 {
-    hipLaunchKernelGGL((hb_twoshot<T, RMAX, EXACT, U, NT>), dim3(grid), dim3(threads), 0, stream, p);
+    hipLaunchKernelGGL((hb_twoshot<T, RMAX, EXACT, U, NT, NODE>), dim3(grid), dim3(threads), 0,
+                       stream, p);
     return hipGetLastError();
+}
+
+// The hierarchical order, at one vector per lane.  Node sizes 2, 4, 8 and 16
+// on the exact rank tables are compiled as constants; any other shape takes
+// the node size at run time (same results, more instructions).
+template <typename T, int RMAX, bool EXACT, bool NT>
+hipError_t launch_grouped(const HBParams<RMAX> &p, uint32_t grid, uint32_t threads,
+                          hipStream_t stream)
+{
+    if constexpr (EXACT) {
+        if constexpr (RMAX > 2)
+            if (p.group == 2)
+                return launch_one<T, RMAX, true, 1, NT, 2>(p, grid, threads, stream);
+        if constexpr (RMAX > 4)
+            if (p.group == 4)
+                return launch_one<T, RMAX, true, 1, NT, 4>(p, grid, threads, stream);
+        if constexpr (RMAX > 8)
+            if (p.group == 8)
+                return launch_one<T, RMAX, true, 1, NT, 8>(p, grid, threads, stream);
+        if constexpr (RMAX > 16)
+            if (p.group == 16)
+                return launch_one<T, RMAX, true, 1, NT, 16>(p, grid, threads, stream);
+    }
+    return launch_one<T, RMAX, EXACT, 1, NT, -1>(p, grid, threads, stream);
 }
 
 // Largest vectors-per-lane count compiled for a rank table size (register
@@ -152,6 +211,9 @@ hipError_t launch_unroll(const HBParams<RMAX> &p, uint32_t grid, uint32_t thread
                          bool nt, hipStream_t stream)
 {
     constexpr int kMax = max_unroll(RMAX);
+    if (p.group != 0)
+        return nt ? launch_grouped<T, RMAX, EXACT, true>(p, grid, threads, stream)
+                  : launch_grouped<T, RMAX, EXACT, false>(p, grid, threads, stream);
     if (u >= 4 && kMax >= 4)
         return nt ? launch_one<T, RMAX, EXACT, (kMax >= 4 ? 4 : 1), true>(p, grid, threads, stream)
                   : launch_one<T, RMAX, EXACT, (kMax >= 4 ? 4 : 1), false>(p, grid, threads, stream);
@@ -164,7 +226,7 @@ hipError_t launch_unroll(const HBParams<RMAX> &p, uint32_t grid, uint32_t thread
 
 template <typename T, int RMAX, bool EXACT>
 hipError_t launch_table(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, int want_threads, uint64_t want_blocks,
+                        const arComm *comm, int want_threads, uint64_t want_blocks, int group,
                         hipStream_t stream)
 {
     constexpr uint64_t kPerVec = 16 / T::kBytes;
@@ -178,6 +240,7 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     p.chunk_vec = p.nvec / (uint64_t)nranks;
     p.nranks = (uint32_t)nranks;
     p.interleaved = comm->opt[arOptHBChunkLayout] == 1 ? 1u : 0u;
+    p.group = group > 1 && group < nranks ? (uint32_t)group : 0u;
 
     int u = comm->opt[arOptHBUnroll] > 0 ? (int)comm->opt[arOptHBUnroll] : 1;
     if (u > max_unroll(RMAX))
@@ -208,36 +271,39 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
 
 template <typename T>
 hipError_t launch_dtype(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, int th, uint64_t bl, hipStream_t stream)
+                        const arComm *comm, int th, uint64_t bl, int grp, hipStream_t stream)
 {
     switch (nranks) {
-    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, comm, th, bl, stream);
+    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, comm, th, bl, grp, stream);
     default: break;
     }
     if (nranks < 4)
-        return launch_table<T, 4, false>(send, recv, count, nranks, comm, th, bl, stream);
+        return launch_table<T, 4, false>(send, recv, count, nranks, comm, th, bl, grp, stream);
     if (nranks < 8)
-        return launch_table<T, 8, false>(send, recv, count, nranks, comm, th, bl, stream);
+        return launch_table<T, 8, false>(send, recv, count, nranks, comm, th, bl, grp, stream);
     if (nranks < 16)
-        return launch_table<T, 16, false>(send, recv, count, nranks, comm, th, bl, stream);
-    return launch_table<T, 32, false>(send, recv, count, nranks, comm, th, bl, stream);
+        return launch_table<T, 16, false>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    return launch_table<T, 32, false>(send, recv, count, nranks, comm, th, bl, grp, stream);
 }
 
 }  // namespace
 
 hipError_t launch_hb(const void *const *send, void *const *recv, size_t count, int dtype,
-                     int nranks, const arComm *comm, int threads, uint64_t blocks,
+                     int nranks, const arComm *comm, int threads, uint64_t blocks, int group,
                      hipStream_t stream)
 {
     switch (dtype) {
-    case kBf16: return launch_dtype<Bf16>(send, recv, count, nranks, comm, threads, blocks, stream);
-    case kFp16: return launch_dtype<Fp16>(send, recv, count, nranks, comm, threads, blocks, stream);
-    default: return launch_dtype<Fp32>(send, recv, count, nranks, comm, threads, blocks, stream);
+    case kBf16:
+        return launch_dtype<Bf16>(send, recv, count, nranks, comm, threads, blocks, group, stream);
+    case kFp16:
+        return launch_dtype<Fp16>(send, recv, count, nranks, comm, threads, blocks, group, stream);
+    default:
+        return launch_dtype<Fp32>(send, recv, count, nranks, comm, threads, blocks, group, stream);
     }
 }
 

@@ -102,7 +102,17 @@ typedef enum {
      * contiguous c-th of R equal parts, 1: every R-th tile starting at tile c
      * (default; streams all R buffers in address order, which HBM serves
      * faster). */
-    arOptHBChunkLayout = 8
+    arOptHBChunkLayout = 8,
+    /* HB: hierarchical summation order for groups of this many consecutive
+     * ranks ("nodes"): each node's partial is summed in binary32 in rank order,
+     * then the partials in node order, then rounded once -- the result of a
+     * two-level all-reduce that reduces inside each node first and across
+     * nodes second ("SGLang 中的 MSCCL++ All-Reduce 基准测试与推理集成指南",
+     * section 4.4: multi-node algorithms for TP = 16 / 32).  0 (default), 1
+     * or >= nranks: the flat order 0..R-1.  A value in between must divide
+     * nranks (else arInvalidUsage); LL then returns arUnsupported and
+     * arProtoAuto runs HB. */
+    arOptHBGroup = 9
 } arOption_t;
 
 /* Create a communicator on `device` for groups of up to `maxRanks` (1..32)

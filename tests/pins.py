@@ -450,3 +450,41 @@ def pin_grouped_integer(orc, dtype: str, R: int, group: int, n: int = 4096, seed
     out = orc.allreduce_grouped(x, dtype, group)
     assert_same_bits(out[0], _exact_int_bits(ints.sum(axis=0), dtype), dtype,
                      f"grouped integer {dtype} R={R} g={group}")
+
+
+def check_order_tolerance(x_bits: np.ndarray, y1: np.ndarray, y2: np.ndarray, dtype: str):
+    """Two summation orders of the same inputs agree to the rounding-error bound.
+
+    Each binary32 order is within gamma_{R-1} * sum|x_j| of the exact sum
+    (Higham, Accuracy and Stability of Numerical Algorithms, sec. 4.2), so two
+    orders differ by at most twice that plus one unit in the last place of the
+    output format.  Where the column does not cancel (|sum x| >= sum|x| / 2)
+    that is at most one unit in the last place for bf16/fp16.  Returns the
+    number of elements where the two differ."""
+    R = x_bits.shape[0]
+    fmt = em.FORMATS[dtype]
+    if dtype == "fp32":
+        xv = x_bits.view(np.float32).astype(np.float64)
+        a, b = y1.view(np.float32).astype(np.float64), y2.view(np.float32).astype(np.float64)
+    else:
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+        conv = lambda u: torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).view(tdt).double().numpy()
+        xv, a, b = conv(x_bits), conv(y1), conv(y2)
+    mags = np.abs(xv).sum(axis=0)
+    total = xv.sum(axis=0)
+    u = 2.0 ** -24
+    gamma = (R - 1) * u / (1 - (R - 1) * u)
+    big = np.maximum(np.abs(a), np.abs(b))
+    e = np.maximum(np.floor(np.log2(np.where(big > 0, big, 1.0))), fmt.emin)
+    ulp = np.exp2(e - fmt.mbits)
+    diff = np.abs(a - b)
+    bad = diff > 2 * gamma * mags + ulp
+    assert not bad.any(), f"{int(bad.sum())} elements outside the two-order bound"
+    if dtype != "fp32":
+        well = np.abs(total) >= mags / 2
+        assert np.all(diff[well] <= ulp[well]), "a well-conditioned column differs by > 1 ulp"
+    else:
+        # normwise relative difference against the exact sums
+        rel = np.linalg.norm(a - b) / np.linalg.norm(total)
+        assert rel <= 1e-6, f"fp32 normwise relative difference {rel:.3g} > 1e-6"
+    return int((diff > 0).sum())

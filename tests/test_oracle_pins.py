@@ -128,3 +128,26 @@ def test_grouped_orders_really_differ(orc):
     flat = orc.allreduce(x, "fp32")
     grouped = orc.allreduce_grouped(x, "fp32", 8)
     assert int((flat[0].view(np.uint32) != grouped[0].view(np.uint32)).sum()) > 100
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_flat_and_grouped_orders_agree_to_the_rounding_bound(orc, dtype):
+    rng = np.random.default_rng(5)
+    lo, hi = (-12, 12) if dtype != "fp16" else (-12, 10)
+    xb = pins.random_bits(rng, dtype, (32, 100_000), emin=lo, emax=hi)
+    x = xb.view(np.float32) if dtype == "fp32" else xb
+    flat = pins.bits_of(orc.allreduce(x, dtype, nthreads=4), dtype)[0]
+    grouped = pins.bits_of(orc.allreduce_grouped(x, dtype, 8, nthreads=4), dtype)[0]
+    assert pins.check_order_tolerance(xb, flat, grouped, dtype) > 0
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_grouped_degenerate_groups_are_the_flat_order(orc, dtype):
+    # nodes of one rank, or one node of every rank, add in the flat order 0..R-1
+    rng = np.random.default_rng(21)
+    xb = pins.random_bits(rng, dtype, (12, 5000), emin=-12, emax=12)
+    x = xb.view(np.float32) if dtype == "fp32" else xb
+    flat = pins.bits_of(orc.allreduce(x, dtype), dtype)
+    for g in (1, 12):
+        same = pins.bits_of(orc.allreduce_grouped(x, dtype, g), dtype)
+        pins.assert_same_bits(same[0], flat[0], dtype, f"group {g}")
