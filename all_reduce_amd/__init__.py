@@ -56,9 +56,16 @@ class arOption(IntEnum):
     arOptHBThreads = 7
     arOptHBChunkLayout = 8
     arOptHBGroup = 9
+    arOptLLPacketBytes = 10
 
 
 AR_MAX_RANKS = 32
+
+
+class arTunedShape(ctypes.Structure):
+    """Mirror of arTunedShape_t."""
+    _fields_ = [("tuned", ctypes.c_int), ("threads", ctypes.c_int), ("blocks", ctypes.c_int),
+                ("packetBytes", ctypes.c_int), ("us", ctypes.c_float)]
 
 
 class ArError(RuntimeError):
@@ -88,8 +95,7 @@ def library() -> ctypes.CDLL:
         "arCommGetOption": ([vp, i32, ctypes.POINTER(i64)], i32),
         "arAllReduce": ([ctypes.POINTER(vp), ctypes.POINTER(vp), sz, i32, i32, i32, i32, vp, vp], i32),
         "arCommTune": ([vp, i32, i32, sz, vp], i32),
-        "arCommGetTunedShape": ([vp, i32, i32, i32, sz, ctypes.POINTER(i32), ctypes.POINTER(i32),
-                                 ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float)], i32),
+        "arCommGetTunedShape": ([vp, i32, i32, i32, sz, i32, ctypes.POINTER(arTunedShape)], i32),
         "arGetErrorString": ([i32], ctypes.c_char_p),
         "arGetVersion": ([], i32),
     }
@@ -146,13 +152,13 @@ def arCommTune(comm, dtype: int, nranks: int, max_bytes_per_rank: int, stream) -
     return library().arCommTune(comm, int(dtype), nranks, max_bytes_per_rank, stream)
 
 
-def arCommGetTunedShape(comm, dtype: int, nranks: int, protocol: int, bytes_per_rank: int):
-    """Returns (result code, tuned, threads, blocks, microseconds)."""
-    v, t, b, u = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_float(0.0)
+def arCommGetTunedShape(comm, dtype: int, nranks: int, protocol: int, bytes_per_rank: int,
+                        in_place: int = 0):
+    """Returns (result code, arTunedShape)."""
+    shape = arTunedShape()
     r = library().arCommGetTunedShape(comm, int(dtype), nranks, int(protocol), bytes_per_rank,
-                                      ctypes.byref(v), ctypes.byref(t), ctypes.byref(b),
-                                      ctypes.byref(u))
-    return r, v.value, t.value, b.value, u.value
+                                      int(in_place), ctypes.byref(shape))
+    return r, shape
 
 
 def arAllReduce(sendbufs: Sequence[int] | None, recvbufs: Sequence[int] | None, count: int,
@@ -259,14 +265,16 @@ class Comm:
         if r != 0:
             raise ArError(r, "arCommTune")
 
-    def tuned_shape(self, dtype, nranks: int, protocol, bytes_per_rank: int):
-        """(threads, blocks, us) stored for that size -- (0, 0, us) when the
-        built-in default won -- or None if never tuned."""
-        r, v, t, b, u = arCommGetTunedShape(self.handle, dtype_code(dtype), nranks,
-                                            protocol_code(protocol), bytes_per_rank)
+    def tuned_shape(self, dtype, nranks: int, protocol, bytes_per_rank: int,
+                    in_place: bool = False):
+        """(threads, blocks, us, packet_bytes) stored for that size and mode --
+        threads and blocks 0 when the built-in default won; packet_bytes 8 or 16
+        for LL, 0 for HB -- or None if never tuned."""
+        r, s = arCommGetTunedShape(self.handle, dtype_code(dtype), nranks,
+                                   protocol_code(protocol), bytes_per_rank, 1 if in_place else 0)
         if r != 0:
             raise ArError(r, "arCommGetTunedShape")
-        return None if v == 0 else (t, b, u)
+        return None if s.tuned == 0 else (s.threads, s.blocks, s.us, s.packetBytes)
 
     def reset(self, stream=None):
         r = arCommReset(self.handle, self._stream(stream))

@@ -61,6 +61,7 @@ constexpr int64_t kDefaults[kOptionCount] = {
     0,        // arOptHBThreads (auto)
     1,        // arOptHBChunkLayout (interleaved tiles)
     0,        // arOptHBGroup (flat order)
+    0,        // arOptLLPacketBytes (tuned, else 8)
 };
 
 // Argument checks shared by every protocol.  No HIP call.
@@ -125,13 +126,13 @@ bool ll_possible(const arComm *comm, int nranks, size_t bytes)
 
 // The protocol a call runs: arProtoAuto resolves to the tuned faster one.
 arProtocol_t resolve_protocol(const arComm *comm, arDataType_t dtype, int nranks, size_t bytes,
-                              arProtocol_t protocol)
+                              int in_place, arProtocol_t protocol)
 {
     if (protocol != arProtoAuto)
         return protocol;
     const int b = bucket_of(bytes);
-    const ar::TunedShape &ll = comm->tuned[dtype][nranks][arProtoLL][b];
-    const ar::TunedShape &hb = comm->tuned[dtype][nranks][arProtoHB][b];
+    const ar::TunedShape &ll = comm->tuned[dtype][nranks][arProtoLL][in_place][b];
+    const ar::TunedShape &hb = comm->tuned[dtype][nranks][arProtoHB][in_place][b];
     if (ll_possible(comm, nranks, bytes) && ll.valid && (!hb.valid || ll.us < hb.us))
         return arProtoLL;
     return arProtoHB;
@@ -139,10 +140,11 @@ arProtocol_t resolve_protocol(const arComm *comm, arDataType_t dtype, int nranks
 
 hipError_t launch(const void *const *send, void *const *recv, size_t count, arDataType_t dtype,
                   int nranks, arProtocol_t proto, const arComm *comm, int threads,
-                  uint64_t blocks, int group, hipStream_t stream)
+                  uint64_t blocks, int pkt_bytes, int group, hipStream_t stream)
 {
     return proto == arProtoLL
-               ? ar::launch_ll(send, recv, count, (int)dtype, nranks, comm, threads, blocks, stream)
+               ? ar::launch_ll(send, recv, count, (int)dtype, nranks, comm, threads, blocks,
+                               pkt_bytes, stream)
                : ar::launch_hb(send, recv, count, (int)dtype, nranks, comm, threads, blocks, group,
                                stream);
 }
@@ -231,6 +233,7 @@ arResult_t arCommCreate(arComm_t *comm, int device, int maxRanks, size_t maxLLBy
     const uint64_t words = (maxLLBytesPerRank + 3) / 4;
     c->pkt_stride = (words + 31) / 32 * 32;
     const size_t pkt_bytes = (size_t)maxRanks * c->pkt_stride * sizeof(uint64_t);
+    c->ll16_ok = pkt_bytes < ((size_t)1 << 32);
     if (hipMalloc((void **)&c->ctrl, 256) != hipSuccess) {
         delete c;
         return reject(arHipError, "hipMalloc of control words failed");
@@ -311,6 +314,11 @@ arResult_t arCommSetOption(arComm_t comm, arOption_t option, int64_t value)
     case arOptHBThreads: ok = value >= 0 && value <= 1024 && value % 64 == 0; break;
     case arOptHBChunkLayout: ok = value == 0 || value == 1; break;
     case arOptHBGroup: ok = value >= 0 && value <= AR_MAX_RANKS; break;
+    case arOptLLPacketBytes:
+        if (value == 16 && !comm->ll16_ok)
+            return reject(arUnsupported, "16-byte packets need packet memory below 4 GiB");
+        ok = value == 0 || value == 8 || value == 16;
+        break;
     default: return reject(arInvalidArgument, "unknown option");
     }
     if (!ok)
@@ -340,12 +348,15 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
         return reject(arInvalidArgument, "NULL comm");
     const size_t bytes = count * elem_bytes(dtype);
     const int group = hierarchy_group(comm, nranks);
+    int in_place = 1;
+    for (int r = 0; r < nranks; ++r)
+        in_place &= sendbufs[r] == recvbufs[r] ? 1 : 0;
     if (group != 0 && nranks % group != 0)
         return reject(arInvalidUsage, "nranks is not a multiple of arOptHBGroup");
     if (group != 0 && protocol == arProtoLL)
         return reject(arUnsupported, "LL sums in the flat order only (arOptHBGroup is set)");
     const arProtocol_t proto =
-        group != 0 ? arProtoHB : resolve_protocol(comm, dtype, nranks, bytes, protocol);
+        group != 0 ? arProtoHB : resolve_protocol(comm, dtype, nranks, bytes, in_place, protocol);
     if (proto == arProtoLL) {
         if (nranks > comm->max_ranks)
             return reject(arInvalidUsage, "nranks above the communicator's maxRanks");
@@ -356,19 +367,25 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
     if (hipGetDevice(&cur) != hipSuccess || cur != comm->device)
         return reject(arInvalidUsage, "the communicator's device is not the current device");
 
-    // Launch shape: explicit options, else the tuned shape of this size, else
-    // the built-in defaults (0).
-    int threads = (int)comm->opt[proto == arProtoLL ? arOptLLThreads : arOptHBThreads];
-    uint64_t blocks = (uint64_t)comm->opt[proto == arProtoLL ? arOptLLBlocksPerRank : arOptHBBlocks];
-    if (threads == 0 && blocks == 0) {
-        const ar::TunedShape &t = comm->tuned[dtype][nranks][proto][bucket_of(bytes)];
+    // Launch shape: explicit options, else the tuned shape of this size and
+    // mode, else the built-in defaults (0).  A tuned LL entry brings its packet
+    // width with it.
+    const bool ll = proto == arProtoLL;
+    int threads = (int)comm->opt[ll ? arOptLLThreads : arOptHBThreads];
+    uint64_t blocks = (uint64_t)comm->opt[ll ? arOptLLBlocksPerRank : arOptHBBlocks];
+    int pkt = ll ? (int)comm->opt[arOptLLPacketBytes] : 0;
+    if (threads == 0 && blocks == 0 && pkt == 0) {
+        const ar::TunedShape &t = comm->tuned[dtype][nranks][proto][in_place][bucket_of(bytes)];
         if (t.valid) {
             threads = t.threads;
             blocks = (uint64_t)t.blocks;
+            pkt = t.pkt_bytes;
         }
     }
+    if (pkt != 16 || !comm->ll16_ok)
+        pkt = 8;
     const hipError_t e = launch(sendbufs, recvbufs, count, dtype, nranks, proto, comm, threads,
-                                blocks, group, (hipStream_t)stream);
+                                blocks, pkt, group, (hipStream_t)stream);
     if (e != hipSuccess)
         return reject(arHipError, hipGetErrorString(e));
     return arSuccess;
@@ -427,24 +444,32 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype, int nranks, size_t maxB
         const double est_us = (double)(2 * (size_t)nranks * bytes) / 5.0e3 + 3.0;
         int calls = (int)(200.0 / est_us);
         calls = calls < 5 ? 5 : (calls > 20 ? 20 : calls);
-        for (int proto = arProtoLL; proto <= arProtoHB && result == arSuccess; ++proto) {
+        for (int m = 0; m < 4 && result == arSuccess; ++m) {
+            const int proto = m / 2 == 0 ? arProtoLL : arProtoHB;
+            const int in_place = m % 2;  // in place: the send plane is also the receive plane
+            void *const *dst = in_place ? const_cast<void *const *>(send.data()) : recv.data();
             if (proto == arProtoLL && !ll_possible(comm, nranks, bytes))
                 continue;
+            // LL: each packet width gets the default shape and the grid; HB: one pass.
             const int nb = proto == arProtoLL ? 7 : 3;
-            ar::TunedShape best = {0, 0, 0, 0.0f};
-            for (int c = -1; c < 3 * nb && result == arSuccess; ++c) {
+            const int per_width = 1 + 3 * nb;
+            const int widths = proto == arProtoLL ? (comm->ll16_ok ? 2 : 1) : 1;
+            ar::TunedShape best = {0, 0, 0, 0, 0.0f};
+            for (int cw = 0; cw < widths * per_width && result == arSuccess; ++cw) {
+                const int c = cw % per_width - 1;
+                const int pkt = proto == arProtoLL ? (cw / per_width == 0 ? 8 : 16) : 0;
                 const int th = c < 0 ? 0 : (proto == arProtoLL ? kLLThreads[c / nb] : kHBThreads[c / nb]);
                 const int bl = c < 0 ? 0 : (proto == arProtoLL ? kLLBlocks[c % nb] : hb_blocks[c % nb]);
                 float us = 0.0f;
                 hipError_t e = hipSuccess;
                 for (int i = 0; i < 2 && e == hipSuccess; ++i)
-                    e = launch(send.data(), recv.data(), count, dtype, nranks,
-                               (arProtocol_t)proto, comm, th, (uint64_t)bl, 0, st);
+                    e = launch(send.data(), dst, count, dtype, nranks,
+                               (arProtocol_t)proto, comm, th, (uint64_t)bl, pkt, 0, st);
                 for (int rep = 0; rep < 2 && e == hipSuccess; ++rep) {
                     e = hipEventRecord(e0, st);
                     for (int i = 0; i < calls && e == hipSuccess; ++i)
-                        e = launch(send.data(), recv.data(), count, dtype, nranks,
-                                   (arProtocol_t)proto, comm, th, (uint64_t)bl, 0, st);
+                        e = launch(send.data(), dst, count, dtype, nranks,
+                                   (arProtocol_t)proto, comm, th, (uint64_t)bl, pkt, 0, st);
                     if (e == hipSuccess)
                         e = hipEventRecord(e1, st);
                     if (e == hipSuccess)
@@ -461,10 +486,10 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype, int nranks, size_t maxB
                     break;
                 }
                 if (!best.valid || us < 0.97f * best.us)
-                    best = {1, th, bl, us};
+                    best = {1, th, bl, pkt, us};
             }
             if (result == arSuccess)
-                comm->tuned[dtype][nranks][proto][b] = best;
+                comm->tuned[dtype][nranks][proto][in_place][b] = best;
         }
     }
     if (e0 != nullptr)
@@ -486,21 +511,22 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype, int nranks, size_t maxB
 }
 
 arResult_t arCommGetTunedShape(arComm_t comm, arDataType_t dtype, int nranks,
-                               arProtocol_t protocol, size_t bytesPerRank, int *tuned,
-                               int *threads, int *blocks, float *us)
+                               arProtocol_t protocol, size_t bytesPerRank, int inPlace,
+                               arTunedShape_t *shape)
 {
-    if (comm == nullptr || tuned == nullptr || threads == nullptr || blocks == nullptr ||
-        us == nullptr)
+    if (comm == nullptr || shape == nullptr)
         return reject(arInvalidArgument, "NULL argument");
     if ((dtype != arBfloat16 && dtype != arFloat16 && dtype != arFloat32) || nranks < 1 ||
         nranks > AR_MAX_RANKS || (protocol != arProtoLL && protocol != arProtoHB) ||
-        bytesPerRank == 0)
+        bytesPerRank == 0 || (inPlace != 0 && inPlace != 1))
         return reject(arInvalidArgument, "argument out of range");
-    const ar::TunedShape &t = comm->tuned[dtype][nranks][protocol][bucket_of(bytesPerRank)];
-    *tuned = t.valid;
-    *threads = t.threads;
-    *blocks = t.blocks;
-    *us = t.us;
+    const ar::TunedShape &t =
+        comm->tuned[dtype][nranks][protocol][inPlace][bucket_of(bytesPerRank)];
+    shape->tuned = t.valid;
+    shape->threads = t.threads;
+    shape->blocks = t.blocks;
+    shape->packetBytes = t.pkt_bytes;
+    shape->us = t.us;
     return arSuccess;
 }
 

@@ -5,6 +5,7 @@
 // all-reduce guide, blog.gitcode.com, section 4.3):
 //
 //  * data moves as 32-bit words (LL packet payloads) or 128-bit vectors (HB);
+//  * the R simulated ranks' buffers reach a kernel as a table of pointers;
 //  * each element is widened to binary32 exactly, summed in rank order
 //    0..R-1 starting from rank 0's value, and narrowed once with round to
 //    nearest even.
@@ -89,22 +90,14 @@ __device__ inline void store16(u32x4 *p, u32x4 v)
         *p = v;
 }
 
-// Packet word of the LL protocol: low 32 bits payload, high 32 bits flag.
-// Written and read as one aligned 64-bit access at agent (device) scope, so
-// payload and flag become visible together to a reader on any XCD.
-__device__ inline void put_packet(uint64_t *slot, uint32_t payload, uint32_t flag)
-{
-    __hip_atomic_store(slot, ((uint64_t)flag << 32) | payload, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ inline uint64_t read_packet(const uint64_t *slot)
-{
-    return __hip_atomic_load(const_cast<uint64_t *>(slot), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ inline uint32_t packet_flag(uint64_t pkt) { return (uint32_t)(pkt >> 32); }
-__device__ inline uint32_t packet_payload(uint64_t pkt) { return (uint32_t)pkt; }
+// Rank pointer table, passed by value in the kernel arguments: the host-built
+// "channels" of the simulated group (the microsoft/mscclpp project summary,
+// agentlenshq.com, "How it works": channels are set up on the host and used
+// from device code).  Sized for the kernel's compile-time rank count.
+template <int R>
+struct RankTable {
+    const void *send[R];
+    void *recv[R];
+};
 
 }  // namespace ar

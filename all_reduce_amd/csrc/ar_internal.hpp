@@ -9,47 +9,6 @@
 
 namespace ar {
 
-// Rank pointer table, passed by value in the kernel arguments: the host-built
-// "channels" of the simulated group (the microsoft/mscclpp project summary,
-// agentlenshq.com, "How it works": channels are set up on the host and used
-// from device code).  Sized for the kernel's compile-time rank count.
-template <int R>
-struct RankTable {
-    const void *send[R];
-    void *recv[R];
-};
-
-// Two-shot HB launch parameters.
-template <int R>
-struct HBParams {
-    RankTable<R> rk;
-    uint64_t nvec;        // whole 16-byte vectors per rank
-    uint64_t chunk_vec;   // vectors per chunk 0..R-2; the last chunk takes the rest
-    uint32_t blocks_per_chunk;
-    uint32_t nranks;      // runtime rank count (the generic kernel; else == R)
-    uint32_t tail_elems;  // elements after the last whole vector
-    uint32_t interleaved; // 0: chunk c = contiguous vectors; 1: tiles c, c+R, c+2R, ...
-    uint32_t group;       // hierarchical order: ranks per node (1 < group < nranks); else 0
-    uint32_t pad;
-};
-
-// One-shot LL launch parameters.
-template <int R>
-struct LLParams {
-    RankTable<R> rk;
-    uint64_t *pkts;          // packet scratch; rank k's packets start at k * pkt_stride
-    uint64_t pkt_stride;
-    uint64_t npkt;           // packets per rank = ceil(bytes per rank / 4)
-    uint64_t put_per_block;  // packets each workgroup publishes for its rank
-    uint64_t get_per_block;  // packets each workgroup polls, reduces and writes out
-    uint32_t *ctrl;          // [0] async error (0 or arTimeout)
-    uint64_t timeout_ticks;  // wall-clock ticks one packet wait may take
-    uint32_t flag_skew;      // test hook: consumers wait for flag + skew
-    uint32_t half_tail;      // 1 when the last packet carries only 2 payload bytes
-    uint32_t nranks;
-    uint32_t blocks_per_rank;
-};
-
 enum DType { kBf16 = 0, kFp16 = 1, kFp32 = 2 };
 
 // Occupancy-derived cap on co-resident LL workgroups: LL consumers wait on
@@ -60,7 +19,7 @@ constexpr int kThreadChoices = 5; // 64, 128, 256, 512, 1024
 
 }  // namespace ar
 
-constexpr int kOptionCount = 10;
+constexpr int kOptionCount = 11;
 
 namespace ar {
 // One tuned launch shape: threads per workgroup and workgroups (HB: the
@@ -70,6 +29,7 @@ struct TunedShape {
     int32_t valid;
     int32_t threads;
     int32_t blocks;
+    int32_t pkt_bytes;  // LL packet width that won: 8 or 16 (HB: 0)
     float us;
 };
 // Message sizes are bucketed by ceil(log2(bytes per rank)).
@@ -86,9 +46,14 @@ struct arComm {
     uint64_t pkt_stride;   // packets per rank region
     uint32_t *ctrl;        // control words; [0] is the async error
     int64_t opt[kOptionCount]; // indexed by arOption_t
-    int ll_resident[3][ar::kRankVariants + 1][ar::kThreadChoices];
-    // [dtype][nranks][protocol][bucket]; filled by arCommTune
-    ar::TunedShape tuned[3][AR_MAX_RANKS + 1][2][ar::kBuckets];
+    // [packet width: 8 B, 16 B][dtype][rank variant][thread-count index]
+    int ll_resident[2][3][ar::kRankVariants + 1][ar::kThreadChoices];
+    bool ll16_ok;          // the packet scratch is small enough for 16-byte packets
+    // [dtype][nranks][protocol][in place][bucket]; filled by arCommTune.  In
+    // place and out of place are tuned apart: on MI355X they favour different
+    // shapes (8 x 128 MiB bf16: 256 x 256 is fastest in place, 512 workgroups
+    // out of place, each about 10 % off on the other).
+    ar::TunedShape tuned[3][AR_MAX_RANKS + 1][2][2][ar::kBuckets];
 };
 
 namespace ar {
@@ -104,8 +69,10 @@ namespace ar {
 hipError_t launch_hb(const void *const *send, void *const *recv, size_t count, int dtype,
                      int nranks, const arComm *comm, int threads, uint64_t blocks, int group,
                      hipStream_t stream);
+// `pkt_bytes` 16 selects 16-byte LL packets (the caller checks comm->ll16_ok),
+// anything else 8-byte packets.
 hipError_t launch_ll(const void *const *send, void *const *recv, size_t count, int dtype,
-                     int nranks, const arComm *comm, int threads, uint64_t blocks,
+                     int nranks, const arComm *comm, int threads, uint64_t blocks, int pkt_bytes,
                      hipStream_t stream);
 hipError_t launch_reset(const arComm *comm, hipStream_t stream);
 // Fills comm->ll_resident from the occupancy calculator.

@@ -27,6 +27,20 @@
 
 namespace ar {
 
+// Two-shot HB launch parameters.
+template <int R>
+struct HBParams {
+    RankTable<R> rk;
+    uint64_t nvec;        // whole 16-byte vectors per rank
+    uint64_t chunk_vec;   // vectors per chunk 0..R-2; the last chunk takes the rest
+    uint32_t blocks_per_chunk;
+    uint32_t nranks;      // runtime rank count (the generic kernel; else == R)
+    uint32_t tail_elems;  // elements after the last whole vector
+    uint32_t interleaved; // 0: chunk c = contiguous vectors; 1: tiles c, c+R, c+2R, ...
+    uint32_t group;       // hierarchical order: ranks per node (1 < group < nranks); else 0
+    uint32_t pad;
+};
+
 // Scalar path for the elements after the last whole 16-byte vector.
 template <typename T>
 __device__ inline float load_elem(const void *base, uint64_t i)

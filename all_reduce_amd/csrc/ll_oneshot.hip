@@ -6,15 +6,16 @@
 // building blocks are a one-sided put of data plus a signal, and a wait on the
 // other side (the microsoft/mscclpp project summary, agentlenshq.com, "How it
 // works": put/signal/wait with no matching receive).  Here put and signal are
-// one 64-bit store: a 4-byte payload next to a 4-byte flag, so a reader that
-// sees the flag also sees the payload, with no separate fence or counter.
+// one store: a 4-byte payload next to a 4-byte flag (an 8-byte packet), or two
+// such pairs in one 16-byte packet, so a reader that sees the flags also sees
+// the payload, with no separate fence or counter.
 //
 // One kernel does the whole call for all R simulated ranks.  Workgroup
 // w = b * R + k acts for rank k on slice b of the message:
 //   put     rank k's words of slice b become packets {payload, ready} in rank
 //           k's packet region (the stand-in for peer memory);
 //   poll    the workgroup takes sub-slice k of slice b and, lane by lane,
-//           re-reads the R packets of each word until all R are ready --
+//           re-reads the R packets of each packet index until all R are ready --
 //           R - 1 of them are written by other workgroups, which for R = 8
 //           sit on the other seven XCDs;
 //   reduce  binary32 sum in rank order 0..R-1, rounded once to the dtype;
@@ -38,47 +39,78 @@
 // (arCommReset) before further LL calls.  Every workgroup of the grid must be
 // resident at once (the host caps the grid with the occupancy calculator),
 // because consumers wait on producers.
-#include "ar_device.hpp"
 #include "ar_internal.hpp"
+#include "ll_packet.hpp"
 
 namespace ar {
 
+// One-shot LL launch parameters.
+template <int R>
+struct LLParams {
+    RankTable<R> rk;
+    uint64_t *pkts;          // packet scratch; rank k's packets start at k * pkt_stride
+    uint64_t pkt_stride;     // packets of this launch's width per rank region
+    uint64_t region_bytes;   // size of the whole packet scratch
+    uint64_t npkt;           // packets per rank = ceil(bytes per rank / payload bytes)
+    uint64_t put_per_block;  // packets each workgroup publishes for its rank
+    uint64_t get_per_block;  // packets each workgroup polls, reduces and writes out
+    uint32_t *ctrl;          // [0] async error (0 or arTimeout)
+    uint64_t timeout_ticks;  // wall-clock ticks one packet wait may take
+    uint32_t flag_skew;      // test hook: consumers wait for flag + skew
+    uint32_t tail_bytes;     // payload bytes of a last, partial packet (0: none)
+    uint32_t nranks;
+    uint32_t blocks_per_rank;
+};
+
 // Largest workgroup compiled for a rank-table size (the polled packets of a
-// lane, 2 VGPRs each, must fit the register share of that many threads).
+// lane, 2 or 4 VGPRs each, must fit the register share of that many threads).
 constexpr int ll_max_threads(int rmax) { return rmax >= 32 ? 512 : 1024; }
-// Words a lane polls at once: R packets each, all loads in flight together.
-constexpr int ll_get_batch(int rmax) { return rmax <= 8 ? 2 : 1; }
-// Source words a lane loads before it stores their packets.
+// Packets a lane polls at once: R packets each, all loads in flight together
+// (the same bytes in flight for both widths).
+constexpr int ll_get_batch(int rmax, int pw) { return rmax * pw <= 8 ? 2 : 1; }
+// Source packets' worth of words a lane loads before it stores their packets.
 constexpr int kPutBatch = 8;
 // Flag of a ready packet; cleared packet memory reads 0.
 constexpr uint32_t kReady = 1u;
 
-template <typename T, int RMAX, bool EXACT>
+// PW: payload words per packet (1: 8-byte packets; 2: 16-byte packets).
+template <typename T, int RMAX, bool EXACT, int PW>
 __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX> p)
 {
-    constexpr int GB = ll_get_batch(RMAX);
+    constexpr int GB = ll_get_batch(RMAX, PW);
+    using IO = PacketIO<PW>;
+    using V = typename IO::V;
+    const IO io(p.pkts, p.region_bytes);
     const uint32_t n = EXACT ? RMAX : p.nranks;
     const uint32_t nthr = blockDim.x;
     const uint32_t k = blockIdx.x % n;
     const uint32_t b = blockIdx.x / n;
 
-    // put: publish rank k's words of slice b
+    // put: publish rank k's packets of slice b
     const uint64_t p0 = (uint64_t)b * p.put_per_block;
     const uint64_t p1 = (p0 + p.put_per_block < p.npkt) ? p0 + p.put_per_block : p.npkt;
     const uint32_t *src = (const uint32_t *)p.rk.send[k];
-    uint64_t *mine = p.pkts + (uint64_t)k * p.pkt_stride;
-    // Whole 4-byte words go through the batches; a message of odd 16-bit
-    // length ends in one 2-byte word, handled by a single lane below.
-    const uint64_t nfull = p.npkt - p.half_tail;
+    const uint64_t mine = (uint64_t)k * p.pkt_stride;
+    // Whole packets go through the batches; a message that ends inside a
+    // packet (2, 4 or 6 bytes of it) has that last packet handled by a single
+    // lane below.
+    const uint64_t nfull = p.npkt - (p.tail_bytes != 0 ? 1 : 0);
     const uint64_t pf = p1 < nfull ? p1 : nfull;
     const uint64_t pstep = (uint64_t)kPutBatch * nthr;
     for (uint64_t pbase = p0 + threadIdx.x; pbase < pf; pbase += pstep) {
-        uint32_t w[kPutBatch];
+        uint32_t w[kPutBatch][PW];
 #pragma unroll
         for (int v = 0; v < kPutBatch; ++v) {
             const uint64_t q = pbase + (uint64_t)v * nthr;
-            if (q < pf)
-                w[v] = src[q];
+            if (q < pf) {
+                if constexpr (PW == 1) {
+                    w[v][0] = src[q];
+                } else {
+                    const uint2 x = ((const uint2 *)src)[q];
+                    w[v][0] = x.x;
+                    w[v][1] = x.y;
+                }
+            }
         }
         // gfx9 counts loads and stores on one counter that runs out of order
         // once both are pending, so a load result needed after a store forces
@@ -89,11 +121,20 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
         for (int v = 0; v < kPutBatch; ++v) {
             const uint64_t q = pbase + (uint64_t)v * nthr;
             if (q < pf)
-                put_packet(mine + q, w[v], kReady);
+                io.store(mine + q, w[v], kReady);
         }
     }
-    if (p.half_tail && threadIdx.x == 0 && nfull >= p0 && nfull < p1)
-        put_packet(mine + nfull, (uint32_t)((const uint16_t *)(src + nfull))[0], kReady);
+    if (p.tail_bytes != 0 && threadIdx.x == 0 && nfull >= p0 && nfull < p1) {
+        // 2 bytes (8-byte packets), or 2, 4 or 6 bytes (16-byte packets)
+        uint32_t w[PW] = {};
+        const uint32_t *t = src + nfull * PW;
+        const bool word = PW == 2 && p.tail_bytes >= 4;
+        if (word)
+            w[0] = t[0];
+        if (p.tail_bytes & 2u)
+            w[word ? 1 : 0] = ((const uint16_t *)t)[word ? 2 : 0];
+        io.store(mine + nfull, w, kReady);
+    }
 
     // poll, reduce, clear, output: sub-slice k of slice b
     const uint32_t want = kReady + p.flag_skew;
@@ -108,7 +149,7 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
     const uint64_t spin_limit = p.timeout_ticks;
     bool gave_up = false;
     for (uint64_t q0 = g0 + threadIdx.x; q0 < g1 && !gave_up; q0 += (uint64_t)GB * nthr) {
-        uint64_t pk[GB][RMAX];
+        V pk[GB][RMAX];
 #pragma unroll
         for (int v = 0; v < GB; ++v) {
             const uint64_t q = q0 + (uint64_t)v * nthr;
@@ -116,7 +157,7 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
 #pragma unroll
                 for (int j = 0; j < RMAX; ++j)
                     if (EXACT || j < (int)n)
-                        pk[v][j] = read_packet(p.pkts + (uint64_t)j * p.pkt_stride + q);
+                        pk[v][j] = io.load((uint64_t)j * p.pkt_stride + q);
             }
         }
         for (;;) {
@@ -127,7 +168,7 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
 #pragma unroll
                     for (int j = 0; j < RMAX; ++j)
                         if (EXACT || j < (int)n)
-                            ready = ready && packet_flag(pk[v][j]) == want;
+                            ready = ready && IO::ready(pk[v][j], want);
             if (ready)
                 break;
             const uint64_t now = wall_clock64();
@@ -145,8 +186,8 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
                 if (q < g1) {
 #pragma unroll
                     for (int j = 0; j < RMAX; ++j)
-                        if ((EXACT || j < (int)n) && packet_flag(pk[v][j]) != want)
-                            pk[v][j] = read_packet(p.pkts + (uint64_t)j * p.pkt_stride + q);
+                        if ((EXACT || j < (int)n) && !IO::ready(pk[v][j], want))
+                            pk[v][j] = io.load((uint64_t)j * p.pkt_stride + q);
                 }
             }
         }
@@ -158,32 +199,43 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
             const uint64_t q = q0 + (uint64_t)v * nthr;
             if (q >= g1)
                 continue;
-            float acc[T::kPerWord];
-            T::widen(packet_payload(pk[v][0]), acc);
+            uint32_t y[PW];
 #pragma unroll
-            for (int j = 1; j < RMAX; ++j) {
-                if (EXACT || j < (int)n) {
-                    float x[T::kPerWord];
-                    T::widen(packet_payload(pk[v][j]), x);
+            for (int e = 0; e < PW; ++e) {
+                float acc[T::kPerWord];
+                T::widen(IO::word(pk[v][0], e), acc);
 #pragma unroll
-                    for (int e = 0; e < T::kPerWord; ++e)
-                        acc[e] = acc[e] + x[e];
+                for (int j = 1; j < RMAX; ++j) {
+                    if (EXACT || j < (int)n) {
+                        float x[T::kPerWord];
+                        T::widen(IO::word(pk[v][j], e), x);
+#pragma unroll
+                        for (int i = 0; i < T::kPerWord; ++i)
+                            acc[i] = acc[i] + x[i];
+                    }
                 }
+                y[e] = T::narrow(acc);
             }
-            const uint32_t y = T::narrow(acc);
 #pragma unroll
             for (int j = 0; j < RMAX; ++j)
                 if (EXACT || j < (int)n)
-                    put_packet(p.pkts + (uint64_t)j * p.pkt_stride + q, 0u, 0u);
-            const bool half = p.half_tail && q == p.npkt - 1;
+                    io.clear((uint64_t)j * p.pkt_stride + q);
+            const bool partial = p.tail_bytes != 0 && q == p.npkt - 1;
 #pragma unroll
             for (int r = 0; r < RMAX; ++r) {
                 if (EXACT || r < (int)n) {
-                    uint32_t *dst = (uint32_t *)p.rk.recv[r] + q;
-                    if (half)
-                        *(uint16_t *)dst = (uint16_t)y;
-                    else
-                        *dst = y;
+                    uint32_t *dst = (uint32_t *)p.rk.recv[r] + q * PW;
+                    if (partial) {
+                        const bool word = PW == 2 && p.tail_bytes >= 4;
+                        if (word)
+                            dst[0] = y[0];
+                        if (p.tail_bytes & 2u)
+                            ((uint16_t *)dst)[word ? 2 : 0] = (uint16_t)y[word ? PW - 1 : 0];
+                    } else if constexpr (PW == 1) {
+                        *dst = y[0];
+                    } else {
+                        *(uint2 *)dst = make_uint2(y[0], y[1]);
+                    }
                 }
             }
         }
@@ -228,7 +280,7 @@ int variant_of(int nranks)
     }
 }
 
-template <typename T, int RMAX, bool EXACT>
+template <typename T, int RMAX, bool EXACT, int PW>
 hipError_t launch_table(const void *const *send, void *const *recv, size_t count, int nranks,
                         const arComm *comm, int want_threads, uint64_t want_blocks,
                         hipStream_t stream)
@@ -239,33 +291,37 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
         p.rk.recv[r] = recv[r];
     }
     const uint64_t bytes = (uint64_t)count * T::kBytes;
-    p.npkt = (bytes + 3) / 4;
-    p.half_tail = (bytes % 4) != 0;
+    const uint64_t words = (bytes + 3) / 4;
+    p.npkt = (bytes + 4 * PW - 1) / (4 * PW);
+    p.tail_bytes = (uint32_t)(bytes % (4 * PW));
     p.pkts = comm->pkts;
-    p.pkt_stride = comm->pkt_stride;
+    p.pkt_stride = comm->pkt_stride / PW;
+    p.region_bytes = (uint64_t)comm->max_ranks * comm->pkt_stride * sizeof(uint64_t);
     p.ctrl = comm->ctrl;
     p.nranks = (uint32_t)nranks;
     p.flag_skew = (uint32_t)comm->opt[arOptDebugFlagSkew];
     p.timeout_ticks = (uint64_t)comm->opt[arOptPollTimeoutUs] * comm->wall_clock_khz / 1000u;
 
-    // Default launch shape, measured on MI355X for R = 8 bf16 from 2 KiB to
-    // 1 MiB per rank: 256-thread workgroups (512 from 512 KiB per rank up),
-    // about two words per lane, at most 64 workgroups per rank (32 from
-    // 256 KiB per rank up).
+    // Default launch shape, measured on MI355X for R = 8 bf16 8-byte packets
+    // from 2 KiB to 1 MiB per rank: 256-thread workgroups (512 from 512 KiB
+    // per rank up), about two words per lane, at most 64 workgroups per rank
+    // (32 from 256 KiB per rank up).  16-byte packets take the same grid, so
+    // each lane moves one packet of two words.
     int threads = want_threads;
     if (threads <= 0)
-        threads = p.npkt >= 131072 ? 512 : 256;
+        threads = words >= 131072 ? 512 : 256;
     if (threads > ll_max_threads(RMAX))
         threads = ll_max_threads(RMAX);
-    const int resident = comm->ll_resident[T::kId][variant_of(nranks)][thread_index(threads)];
+    const int resident =
+        comm->ll_resident[PW - 1][T::kId][variant_of(nranks)][thread_index(threads)];
     uint64_t max_per_rank = (uint64_t)(resident / nranks);
     if (max_per_rank < 1)
         max_per_rank = 1;
 
     uint64_t per_rank = want_blocks;
     if (per_rank == 0) {
-        const uint64_t cap = p.npkt >= 65536 ? 32 : 64;
-        per_rank = (p.npkt + (uint64_t)threads * 2 - 1) / ((uint64_t)threads * 2);
+        const uint64_t cap = words >= 65536 ? 32 : 64;
+        per_rank = (words + (uint64_t)threads * 2 - 1) / ((uint64_t)threads * 2);
         if (per_rank > cap)
             per_rank = cap;
     }
@@ -280,26 +336,34 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     p.blocks_per_rank = (uint32_t)per_rank;
     const uint32_t grid = (uint32_t)(per_rank * (uint64_t)nranks);
 
-    hipLaunchKernelGGL((ll_oneshot<T, RMAX, EXACT>), dim3(grid), dim3(threads), 0, stream, p);
+    hipLaunchKernelGGL((ll_oneshot<T, RMAX, EXACT, PW>), dim3(grid), dim3(threads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, int PW>
 hipError_t launch_dtype(const void *const *send, void *const *recv, size_t count, int nranks,
                         const arComm *comm, int th, uint64_t bl, hipStream_t stream)
 {
     switch (nranks) {
-    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, comm, th, bl, stream);
-    default: return launch_table<T, 32, false>(send, recv, count, nranks, comm, th, bl, stream);
+    case 1: return launch_table<T, 1, true, PW>(send, recv, count, nranks, comm, th, bl, stream);
+    case 2: return launch_table<T, 2, true, PW>(send, recv, count, nranks, comm, th, bl, stream);
+    case 4: return launch_table<T, 4, true, PW>(send, recv, count, nranks, comm, th, bl, stream);
+    case 8: return launch_table<T, 8, true, PW>(send, recv, count, nranks, comm, th, bl, stream);
+    case 16: return launch_table<T, 16, true, PW>(send, recv, count, nranks, comm, th, bl, stream);
+    case 32: return launch_table<T, 32, true, PW>(send, recv, count, nranks, comm, th, bl, stream);
+    default: return launch_table<T, 32, false, PW>(send, recv, count, nranks, comm, th, bl, stream);
     }
 }
 
-template <typename T, int RMAX, bool EXACT>
+template <typename T>
+hipError_t launch_width(const void *const *send, void *const *recv, size_t count, int nranks,
+                        const arComm *comm, int th, uint64_t bl, int pkt_bytes, hipStream_t stream)
+{
+    return pkt_bytes == 16 ? launch_dtype<T, 2>(send, recv, count, nranks, comm, th, bl, stream)
+                           : launch_dtype<T, 1>(send, recv, count, nranks, comm, th, bl, stream);
+}
+
+template <typename T, int RMAX, bool EXACT, int PW>
 hipError_t query_one(int *out)
 {
     for (int i = 0; i < kThreadChoices; ++i) {
@@ -309,7 +373,7 @@ hipError_t query_one(int *out)
         }
         int per_cu = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(&ll_oneshot<T, RMAX, EXACT>),
+            &per_cu, reinterpret_cast<const void *>(&ll_oneshot<T, RMAX, EXACT, PW>),
             kThreadOptions[i], 0);
         if (e != hipSuccess)
             return e;
@@ -318,29 +382,32 @@ hipError_t query_one(int *out)
     return hipSuccess;
 }
 
-template <typename T>
+template <typename T, int PW>
 hipError_t query_dtype(int (*tab)[kThreadChoices])
 {
     hipError_t e;
-    if ((e = query_one<T, 1, true>(tab[0])) != hipSuccess) return e;
-    if ((e = query_one<T, 2, true>(tab[1])) != hipSuccess) return e;
-    if ((e = query_one<T, 4, true>(tab[2])) != hipSuccess) return e;
-    if ((e = query_one<T, 8, true>(tab[3])) != hipSuccess) return e;
-    if ((e = query_one<T, 16, true>(tab[4])) != hipSuccess) return e;
-    if ((e = query_one<T, 32, true>(tab[5])) != hipSuccess) return e;
-    return query_one<T, 32, false>(tab[6]);
+    if ((e = query_one<T, 1, true, PW>(tab[0])) != hipSuccess) return e;
+    if ((e = query_one<T, 2, true, PW>(tab[1])) != hipSuccess) return e;
+    if ((e = query_one<T, 4, true, PW>(tab[2])) != hipSuccess) return e;
+    if ((e = query_one<T, 8, true, PW>(tab[3])) != hipSuccess) return e;
+    if ((e = query_one<T, 16, true, PW>(tab[4])) != hipSuccess) return e;
+    if ((e = query_one<T, 32, true, PW>(tab[5])) != hipSuccess) return e;
+    return query_one<T, 32, false, PW>(tab[6]);
 }
 
 }  // namespace
 
 hipError_t launch_ll(const void *const *send, void *const *recv, size_t count, int dtype,
-                     int nranks, const arComm *comm, int threads, uint64_t blocks,
+                     int nranks, const arComm *comm, int threads, uint64_t blocks, int pkt_bytes,
                      hipStream_t stream)
 {
     switch (dtype) {
-    case kBf16: return launch_dtype<Bf16>(send, recv, count, nranks, comm, threads, blocks, stream);
-    case kFp16: return launch_dtype<Fp16>(send, recv, count, nranks, comm, threads, blocks, stream);
-    default: return launch_dtype<Fp32>(send, recv, count, nranks, comm, threads, blocks, stream);
+    case kBf16:
+        return launch_width<Bf16>(send, recv, count, nranks, comm, threads, blocks, pkt_bytes, stream);
+    case kFp16:
+        return launch_width<Fp16>(send, recv, count, nranks, comm, threads, blocks, pkt_bytes, stream);
+    default:
+        return launch_width<Fp32>(send, recv, count, nranks, comm, threads, blocks, pkt_bytes, stream);
     }
 }
 
@@ -359,15 +426,19 @@ hipError_t launch_reset(const arComm *comm, hipStream_t stream)
 
 hipError_t query_ll_residency(arComm *comm)
 {
-    int per_cu[3][kRankVariants + 1][kThreadChoices] = {};
+    int per_cu[2][3][kRankVariants + 1][kThreadChoices] = {};
     hipError_t e;
-    if ((e = query_dtype<Bf16>(per_cu[kBf16])) != hipSuccess) return e;
-    if ((e = query_dtype<Fp16>(per_cu[kFp16])) != hipSuccess) return e;
-    if ((e = query_dtype<Fp32>(per_cu[kFp32])) != hipSuccess) return e;
-    for (int d = 0; d < 3; ++d)
-        for (int v = 0; v <= kRankVariants; ++v)
-            for (int t = 0; t < kThreadChoices; ++t)
-                comm->ll_resident[d][v][t] = per_cu[d][v][t] * comm->cu_count;
+    if ((e = query_dtype<Bf16, 1>(per_cu[0][kBf16])) != hipSuccess) return e;
+    if ((e = query_dtype<Fp16, 1>(per_cu[0][kFp16])) != hipSuccess) return e;
+    if ((e = query_dtype<Fp32, 1>(per_cu[0][kFp32])) != hipSuccess) return e;
+    if ((e = query_dtype<Bf16, 2>(per_cu[1][kBf16])) != hipSuccess) return e;
+    if ((e = query_dtype<Fp16, 2>(per_cu[1][kFp16])) != hipSuccess) return e;
+    if ((e = query_dtype<Fp32, 2>(per_cu[1][kFp32])) != hipSuccess) return e;
+    for (int w = 0; w < 2; ++w)
+        for (int d = 0; d < 3; ++d)
+            for (int v = 0; v <= kRankVariants; ++v)
+                for (int t = 0; t < kThreadChoices; ++t)
+                    comm->ll_resident[w][d][v][t] = per_cu[w][d][v][t] * comm->cu_count;
     return hipSuccess;
 }
 

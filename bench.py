@@ -297,8 +297,10 @@ def main():
             row["torch_eager_us"] = round(B.eager_us(B.torch_fn(sv, rv)), 3)
             for proto in ("ll", "hb"):
                 shape = B.comm.tuned_shape(torch.bfloat16, R, proto, 2 * n)
-                row[f"{proto}_shape"] = (("default" if shape[0] == 0 else list(shape[:2]))
-                                         if shape else None)
+                row[f"{proto}_shape"] = (("default" if shape[0] == 0 and shape[1] == 0
+                                          else list(shape[:2])) if shape else None)
+            shape = B.comm.tuned_shape(torch.bfloat16, R, "ll", 2 * n)
+            row["ll_packet_bytes"] = shape[3] if shape else 8
             sweep_rows.append(row)
             log(f"sweep 2^{k}: LL {row['ll_us']:.2f} us  HB {row['hb_us']:.2f} us (graph); "
                 f"eager LL {row['ll_eager_us']:.2f} HB {row['hb_eager_us']:.2f} "
@@ -351,6 +353,9 @@ def main():
         pre["us_per_launch"] = round(avg_us, 2)
         pre["gbps"] = gbps(R, n, 2, avg_us)
         pre["gbps_cold"] = gbps(R, n, 2, mean_us)
+        shape = B.comm.tuned_shape(torch.bfloat16, R, "hb", 2 * n, in_place=True)
+        pre["shape"] = (("default" if shape[0] == 0 and shape[1] == 0 else list(shape[:2]))
+                        if shape else None)
         result["hb_prefill"] = pre
         traffic = _counter_traffic()
         result["roofline"] = {
@@ -591,13 +596,17 @@ def run_configs(B, inputs, sweep_rows, result):
 
 
 def _sources_digest() -> str:
-    """sha256 over the HB kernel's sources, to tie counter readings to them."""
+    """sha256 over what the HB kernel is compiled from (its source file, the
+    device header it includes, the compiler flags without include paths), to
+    tie counter readings to that kernel."""
     import hashlib
     from pathlib import Path
+    from all_reduce_amd import build
     csrc = Path(__file__).resolve().parent / "all_reduce_amd" / "csrc"
     h = hashlib.sha256()
-    for name in ("hb_twoshot.hip", "ar_device.hpp", "ar_internal.hpp"):
+    for name in ("hb_twoshot.hip", "ar_device.hpp"):
         h.update((csrc / name).read_bytes())
+    h.update(" ".join(f for f in build.HIP_FLAGS if not f.startswith("-I")).encode())
     return h.hexdigest()
 
 

@@ -112,14 +112,21 @@ typedef enum {
      * or >= nranks: the flat order 0..R-1.  A value in between must divide
      * nranks (else arInvalidUsage); LL then returns arUnsupported and
      * arProtoAuto runs HB. */
-    arOptHBGroup = 9
+    arOptHBGroup = 9,
+    /* LL: packet width in bytes.  8: a 4-byte payload next to a 4-byte flag;
+     * 16: two such pairs, written and read as one 16-byte access (half the
+     * memory instructions per payload byte).  0 (default): the width the
+     * tuner chose for the message size, else 8.  16 needs the communicator's
+     * packet memory below 4 GiB (maxRanks * maxLLBytesPerRank * 2), else
+     * setting it returns arUnsupported. */
+    arOptLLPacketBytes = 10
 } arOption_t;
 
 /* Create a communicator on `device` for groups of up to `maxRanks` (1..32)
  * simulated ranks and LL messages of up to `maxLLBytesPerRank` bytes per rank.
  * It owns device memory for the LL packets (2 * maxRanks * maxLLBytesPerRank
- * bytes, each 4-byte payload travels in an 8-byte packet; all zero between
- * calls) and a word that records an asynchronous error.  maxLLBytesPerRank
+ * bytes: packets are half payload, half flags, at either width; all zero
+ * between calls) and a word that records an asynchronous error.  maxLLBytesPerRank
  * may be 0 (HB only).  Allocates with hipMalloc, so it must not be called
  * while a stream is being captured.  The caller's current device is left
  * unchanged.
@@ -155,12 +162,14 @@ arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
  *
  * For `dtype` and `nranks`, every power-of-two size from 512 bytes up to
  * maxBytesPerRank per rank (the last bucket at maxBytesPerRank itself) is
- * timed with each protocol the communicator can run at that size, over the
- * built-in default shape and a fixed set of candidates; a candidate wins only
- * if it is more than 3 % faster than the best before it, and the winner and
- * its time are stored in the communicator.  Later calls of that dtype and rank count use the stored
- * shape of their size bucket (the message size rounded up to a power of two)
- * unless arOptLLThreads/arOptLLBlocksPerRank (LL) or arOptHBThreads/
+ * timed with each protocol the communicator can run at that size, in place
+ * and out of place (the two favour different shapes), over the built-in
+ * default shape and a fixed set of candidates; a candidate wins only if it is
+ * more than 3 % faster than the best before it, and the winner and its time
+ * are stored in the communicator.  Later calls of that dtype and rank count
+ * use the stored shape of their size bucket (the message size rounded up to a
+ * power of two) and mode (in place: recvbufs[r] == sendbufs[r] for every
+ * rank) unless arOptLLThreads/arOptLLBlocksPerRank (LL) or arOptHBThreads/
  * arOptHBBlocks (HB) are set; arProtoAuto then picks the faster protocol.
  * Tuning again overwrites the table; sizes never tuned use built-in defaults.
  *
@@ -174,15 +183,22 @@ arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
 arResult_t arCommTune(arComm_t comm, arDataType_t dtype, int nranks, size_t maxBytesPerRank,
                       arStream_t stream);
 
-/* The tuned shape for (dtype, nranks, protocol LL or HB) at a message of
- * bytesPerRank bytes.  *tuned = 0 when that size was never tuned.  Otherwise
- * *threads and *blocks are the threads per workgroup and workgroups (HB: the
- * grid; LL: per rank) that won -- both 0 when the built-in default shape won --
- * and *us the time per call measured for it, in microseconds.  Returns
- * arInvalidArgument for NULL pointers or out-of-range arguments. */
+/* One entry of the tuned table. */
+typedef struct {
+    int tuned;        /* 0: this size was never tuned (the rest is 0) */
+    int threads;      /* threads per workgroup that won; 0 with blocks 0: the default shape */
+    int blocks;       /* workgroups that won (HB: the grid; LL: per rank) */
+    int packetBytes;  /* LL: the packet width that won, 8 or 16; HB: 0 */
+    float us;         /* time per call measured for it, in microseconds */
+} arTunedShape_t;
+
+/* The tuned entry for (dtype, nranks, protocol LL or HB) at a message of
+ * bytesPerRank bytes, in place (inPlace = 1) or out of place (inPlace = 0),
+ * copied to *shape.  Returns arInvalidArgument for NULL pointers or
+ * out-of-range arguments. */
 arResult_t arCommGetTunedShape(arComm_t comm, arDataType_t dtype, int nranks,
-                               arProtocol_t protocol, size_t bytesPerRank, int *tuned,
-                               int *threads, int *blocks, float *us);
+                               arProtocol_t protocol, size_t bytesPerRank, int inPlace,
+                               arTunedShape_t *shape);
 
 /* The sum all-reduce.
  *

@@ -1,9 +1,10 @@
 """Calls captured in a HIP graph and replayed (through torch.cuda.CUDAGraph).
 
-Replays freeze the kernel arguments, so the LL packet flags must come from the
-device-side epoch: two inputs alternating in one graph would read each other's
-stale packets otherwise.  Every replay is checked against the oracle, with
-eager calls and synchronisations between replays.
+Replays freeze the kernel arguments, so nothing in an LL call may depend on a
+per-call value from the host: packet memory must be clean after every call,
+or two inputs alternating in one graph would read each other's stale packets.
+Every replay is checked against the oracle, with eager calls and
+synchronisations between replays.
 """
 import pytest
 import torch
@@ -74,7 +75,7 @@ def test_graph_alternating_inputs(comm, orc, protocol, N):
         torch.cuda.synchronize()
         assert_parity(torch.stack([t.cpu() for t in da]), want_a, f"replay {rep} A")
         assert_parity(torch.stack([t.cpu() for t in db]), want_b, f"replay {rep} B")
-        # eager work of another size between replays advances the epoch too
+        # eager work of another size between replays uses the same packet memory
         from gpu_util import run_allreduce
         assert_parity(run_allreduce(comm, x_small, protocol), expect(orc, x_small), "eager")
     assert comm.async_error() == ar.arResult.arSuccess

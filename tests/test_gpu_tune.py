@@ -2,7 +2,8 @@
 
 Tuning only changes launch shapes, so every result must stay bit-exact with
 the oracle; the tuned table must cover every power-of-two size it was asked
-for, for each protocol the communicator can run there.
+for, in place and out of place, for each protocol the communicator can run
+there.
 """
 import pytest
 import torch
@@ -26,11 +27,12 @@ def comm():
     c.close()
 
 
-def test_table_covers_the_tuned_sizes(comm):
+@pytest.mark.parametrize("in_place", [False, True])
+def test_table_covers_the_tuned_sizes(comm, in_place):
     for b in range(9, 23):
-        hb = comm.tuned_shape(torch.bfloat16, 8, "hb", 1 << b)
+        hb = comm.tuned_shape(torch.bfloat16, 8, "hb", 1 << b, in_place)
         assert hb is not None and hb[0] in (0, 128, 256, 512) and hb[2] > 0
-        ll = comm.tuned_shape(torch.bfloat16, 8, "ll", 1 << b)
+        ll = comm.tuned_shape(torch.bfloat16, 8, "ll", 1 << b, in_place)
         if (1 << b) <= comm.max_ll_bytes_per_rank:
             assert ll is not None and ll[0] in (0, 256, 512, 1024) and ll[2] > 0
         else:
@@ -43,13 +45,20 @@ def test_table_covers_the_tuned_sizes(comm):
     assert comm.tuned_shape(torch.float32, 16, "ll", 1 << 18) is not None
 
 
+@pytest.mark.parametrize("in_place", [False, True])
 @pytest.mark.parametrize("protocol", ["ll", "hb", "auto"])
 @pytest.mark.parametrize("k", [10, 13, 16, 19, 21])
-def test_tuned_shapes_keep_bits(comm, orc, protocol, k):
+def test_tuned_shapes_keep_bits(comm, orc, protocol, k, in_place):
     if protocol == "ll" and ((1 << k) + 3) * 2 > comm.max_ll_bytes_per_rank:
         pytest.skip("above the communicator's LL limit")
     x = inputs.make(8, (1 << k) + 3, "bf16", "outliers", seed=60 + k)
-    assert_parity(run_allreduce(comm, x, protocol), expect(orc, x), f"tuned {protocol} 2^{k}")
+    assert_parity(run_allreduce(comm, x, protocol, inplace=in_place), expect(orc, x),
+                  f"tuned {protocol} 2^{k} in_place={in_place}")
+
+
+def test_mode_argument_is_checked(comm):
+    r = ar.arCommGetTunedShape(comm.handle, 0, 8, 1, 4096, 2)[0]
+    assert r == ar.arResult.arInvalidArgument
 
 
 def test_auto_on_untuned_sizes_and_fp32(comm, orc):
