@@ -57,6 +57,7 @@ class arOption(IntEnum):
     arOptHBChunkLayout = 8
     arOptHBGroup = 9
     arOptLLPacketBytes = 10
+    arOptHBStaged = 11
 
 
 AR_MAX_RANKS = 32

@@ -62,6 +62,7 @@ constexpr int64_t kDefaults[kOptionCount] = {
     1,        // arOptHBChunkLayout (interleaved tiles)
     0,        // arOptHBGroup (flat order)
     0,        // arOptLLPacketBytes (tuned, else 8)
+    0,        // arOptHBStaged (fused)
 };
 
 // Argument checks shared by every protocol.  No HIP call.
@@ -314,6 +315,7 @@ arResult_t arCommSetOption(arComm_t comm, arOption_t option, int64_t value)
     case arOptHBThreads: ok = value >= 0 && value <= 1024 && value % 64 == 0; break;
     case arOptHBChunkLayout: ok = value == 0 || value == 1; break;
     case arOptHBGroup: ok = value >= 0 && value <= AR_MAX_RANKS; break;
+    case arOptHBStaged: ok = value == 0 || value == 1; break;
     case arOptLLPacketBytes:
         if (value == 16 && !comm->ll16_ok)
             return reject(arUnsupported, "16-byte packets need packet memory below 4 GiB");
@@ -355,6 +357,9 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
         return reject(arInvalidUsage, "nranks is not a multiple of arOptHBGroup");
     if (group != 0 && protocol == arProtoLL)
         return reject(arUnsupported, "LL sums in the flat order only (arOptHBGroup is set)");
+    const bool staged = comm->opt[arOptHBStaged] != 0;
+    if (group != 0 && staged)
+        return reject(arUnsupported, "the staged HB form sums in the flat order only");
     const arProtocol_t proto =
         group != 0 ? arProtoHB : resolve_protocol(comm, dtype, nranks, bytes, in_place, protocol);
     if (proto == arProtoLL) {
@@ -384,8 +389,15 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
     }
     if (pkt != 16 || !comm->ll16_ok)
         pkt = 8;
-    const hipError_t e = launch(sendbufs, recvbufs, count, dtype, nranks, proto, comm, threads,
-                                blocks, pkt, group, (hipStream_t)stream);
+    // The staged HB form is an ablation: explicit options or its defaults,
+    // never the fused kernel's tuned shape.
+    const hipError_t e =
+        proto == arProtoHB && staged
+            ? ar::launch_hb_staged(sendbufs, recvbufs, count, (int)dtype, nranks, comm,
+                                   (int)comm->opt[arOptHBThreads],
+                                   (uint64_t)comm->opt[arOptHBBlocks], (hipStream_t)stream)
+            : launch(sendbufs, recvbufs, count, dtype, nranks, proto, comm, threads, blocks, pkt,
+                     group, (hipStream_t)stream);
     if (e != hipSuccess)
         return reject(arHipError, hipGetErrorString(e));
     return arSuccess;

@@ -19,7 +19,7 @@ constexpr int kThreadChoices = 5; // 64, 128, 256, 512, 1024
 
 }  // namespace ar
 
-constexpr int kOptionCount = 11;
+constexpr int kOptionCount = 12;
 
 namespace ar {
 // One tuned launch shape: threads per workgroup and workgroups (HB: the
@@ -74,6 +74,11 @@ hipError_t launch_hb(const void *const *send, void *const *recv, size_t count, i
 hipError_t launch_ll(const void *const *send, void *const *recv, size_t count, int dtype,
                      int nranks, const arComm *comm, int threads, uint64_t blocks, int pkt_bytes,
                      hipStream_t stream);
+// The staged form of the HB two-shot (reduce-scatter into the owner's output,
+// kernel boundary, all-gather from it), flat order only.
+hipError_t launch_hb_staged(const void *const *send, void *const *recv, size_t count, int dtype,
+                            int nranks, const arComm *comm, int threads, uint64_t blocks,
+                            hipStream_t stream);
 hipError_t launch_reset(const arComm *comm, hipStream_t stream);
 // Fills comm->ll_resident from the occupancy calculator.
 hipError_t query_ll_residency(arComm *comm);

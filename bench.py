@@ -323,6 +323,14 @@ def main():
         log(f"decode 64x8192: LL {dec['ll_us']:.2f} us  HB {dec['hb_us']:.2f} us")
         del sv, rv
 
+        # The per-call floor of a graph-replayed launch: a one-rank, 16-byte
+        # HB call (one workgroup, one vector), for the latency breakdown.
+        x = inputs.make(1, 8, "bf16", "uniform", seed=0)
+        sv, rv = B.planes(x)
+        result["graph_floor_us"] = round(B.graph_us(sv, rv, 8, "hb"), 3)
+        log(f"graph-replayed launch floor: {result['graph_floor_us']:.2f} us per call")
+        del sv, rv
+
     # ---- HB prefill, in place, 128 MiB per rank -----------------------------
     if args.only in ("all", "prefill"):
         case = inputs.WORKLOADS["C4"]
@@ -582,6 +590,32 @@ def run_configs(B, inputs, sweep_rows, result):
             us, par)
         del x, sv, rv
         log(f"hierarchical R={R} {dtype} done")
+
+    # HB5 ablation: the staged two-shot (reduce-scatter into the owner, kernel
+    # boundary, all-gather from the owner) beside the fused rows above
+    B.comm.set_option(O.arOptHBStaged, 1)
+    try:
+        for name, case, mode in (("C3 64x8192", inputs.WORKLOADS["C3"], "graph"),
+                                 ("C4 8192x8192 in place", inputs.WORKLOADS["C4"], "back-to-back"),
+                                 ("C5b R=32", inputs.integer_case(32, "fp32"), "back-to-back")):
+            x = inputs.make(**case)
+            R, n, dtype = case["nranks"], case["count"], case["dtype"]
+            in_place = "in place" in name
+            sv, rv = B.planes(x)
+            if in_place:
+                rv = sv
+            B.launch(sv, rv, n, "hb")
+            torch.cuda.synchronize()
+            sample = None if n <= (1 << 20) else torch.randint(
+                0, n, (1 << 20,), generator=torch.Generator().manual_seed(97))
+            par = B.parity(x, rv, sample=sample)
+            us = (B.graph_us(sv, rv, n, "hb") if mode == "graph"
+                  else B.back_to_back_us(sv, rv, n, "hb", B.args.steps))
+            add(f"{name} staged", R, dtype, n, "hb", f"{mode}, staged", us, par)
+            del x, sv, rv
+            log(f"staged {name} done")
+    finally:
+        B.comm.set_option(O.arOptHBStaged, 0)
 
     log("\n| config | R | dtype | elems/rank | bytes/rank | proto | mode | µs/call | eff. GB/s | "
         "% of 8 TB/s | oracle ms (1 thr) | oracle ms (T thr) | parity |")

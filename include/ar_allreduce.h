@@ -119,7 +119,17 @@ typedef enum {
      * tuner chose for the message size, else 8.  16 needs the communicator's
      * packet memory below 4 GiB (maxRanks * maxLLBytesPerRank * 2), else
      * setting it returns arUnsupported. */
-    arOptLLPacketBytes = 10
+    arOptLLPacketBytes = 10,
+    /* HB: 1 = the staged two-shot, an ablation of the fused default: the
+     * reduce-scatter writes each reduced chunk to its owner rank's output
+     * only, a kernel boundary stands for the synchronisation between the
+     * shots (the "few syncs" of the HB protocol, "MSCCL++：让 GPU 通信像 CUDA
+     * 一样可编程", "MemoryChannel"), and the all-gather copies each chunk from
+     * its owner to the other outputs.  Same result bits; 2 * bytes per rank
+     * more traffic and one more launch.  Launch shape from arOptHBThreads /
+     * arOptHBBlocks or the defaults, never the tuned table.  With
+     * arOptHBGroup set, HB calls return arUnsupported.  0 (default): fused. */
+    arOptHBStaged = 11
 } arOption_t;
 
 /* Create a communicator on `device` for groups of up to `maxRanks` (1..32)

@@ -1,0 +1,114 @@
+"""The staged HB two-shot (arOptHBStaged = 1), on the GPU.
+
+Reduce-scatter into each chunk owner's output, a kernel boundary, then an
+all-gather from the owner.  The result must be bit-identical to the fused
+kernel and to the oracle: the same rank order and one rounding.
+"""
+import pytest
+import torch
+
+import all_reduce_amd as ar
+from all_reduce_amd import inputs
+from gpu_util import CODES, PROTO, assert_parity, expect, note, run_allreduce
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def comm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    c = ar.Comm(device="cuda:0", max_ranks=32, max_ll_bytes_per_rank=1 << 20)
+    c.set_option(ar.arOption.arOptHBStaged, 1)
+    yield c
+    c.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 13, 16, 32])
+@pytest.mark.parametrize("N", [1, 7, 9, 1029, 262144 + 13])
+def test_matches_oracle(comm, orc, dtype, R, N):
+    x = inputs.make(R, N, dtype, "outliers" if N > 1000 else "normal", seed=4000 + R * 7 + N)
+    assert_parity(run_allreduce(comm, x, "hb"), expect(orc, x), f"staged R={R} N={N} {dtype}")
+
+
+def test_c4_in_place_full_size(comm, orc):
+    x = inputs.make(**inputs.WORKLOADS["C4"])
+    assert_parity(run_allreduce(comm, x, "hb", inplace=True), expect(orc, x), "staged C4")
+
+
+def test_same_bits_as_fused_in_place(comm, orc):
+    x = inputs.make(16, 500_003, "fp16", "outliers", seed=4001)
+    staged = run_allreduce(comm, x, "hb", inplace=True)
+    try:
+        comm.set_option(ar.arOption.arOptHBStaged, 0)
+        fused = run_allreduce(comm, x, "hb", inplace=True)
+    finally:
+        comm.set_option(ar.arOption.arOptHBStaged, 1)
+    assert torch.equal(staged.view(torch.int16), fused.view(torch.int16))
+    assert_parity(staged, expect(orc, x), "staged in place")
+
+
+@pytest.mark.parametrize("opt,values", [
+    (ar.arOption.arOptHBThreads, [64, 512]),
+    (ar.arOption.arOptHBBlocks, [1, 7, 2048]),
+    (ar.arOption.arOptHBNonTemporal, [0, 1]),
+])
+def test_launch_options_keep_bits(comm, orc, opt, values):
+    x = inputs.make(8, 1_000_003, "bf16", "outliers", seed=4002)
+    want = expect(orc, x)
+    old = comm.get_option(opt)
+    try:
+        for v in values:
+            comm.set_option(opt, v)
+            assert_parity(run_allreduce(comm, x, "hb"), want, f"staged {opt.name}={v}")
+    finally:
+        comm.set_option(opt, old)
+
+
+def test_graph_replays(comm, orc):
+    R, N = 8, 300_007
+    x = inputs.make(R, N, "bf16", "normal", seed=4003)
+    want = expect(orc, x)
+    _, sv = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    plane, rv = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    for r in range(R):
+        sv[r].copy_(x[r])
+
+    def call():
+        rc = ar.arAllReduce([t.data_ptr() for t in sv], [t.data_ptr() for t in rv], N,
+                            CODES["bf16"], ar.arRedOp.arSum, R, PROTO["hb"], comm.handle,
+                            torch.cuda.current_stream().cuda_stream)
+        assert rc == ar.arResult.arSuccess, ar.arGetErrorString(rc)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(3):
+            call()
+    for rep in range(3):
+        note(f"staged graph replay {rep}")
+        plane.view(torch.uint8).fill_(0xA5)
+        g.replay()
+        torch.cuda.synchronize()
+        assert_parity(torch.stack([t.cpu() for t in rv]), want, f"staged replay {rep}")
+
+
+def test_hierarchical_order_is_refused(comm):
+    y = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
+    q = [t.data_ptr() for t in y]
+    s = torch.cuda.current_stream().cuda_stream
+    comm.set_option(ar.arOption.arOptHBGroup, 8)
+    try:
+        assert ar.arAllReduce(q, q, 64, 0, 0, 16, 1, comm.handle, s) == ar.arResult.arUnsupported
+    finally:
+        comm.set_option(ar.arOption.arOptHBGroup, 0)
+    assert ar.arAllReduce(q, q, 64, 0, 0, 16, 1, comm.handle, s) == ar.arResult.arSuccess
+    torch.cuda.synchronize()
+    with pytest.raises(ar.ArError):
+        comm.set_option(ar.arOption.arOptHBStaged, 2)
