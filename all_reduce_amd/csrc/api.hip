@@ -150,6 +150,56 @@ hipError_t launch(const void *const *send, void *const *recv, size_t count, arDa
                                stream);
 }
 
+// Per-call time of one tuning candidate: `calls` launches captured into a HIP
+// graph on the tuner's private stream, one warm-up replay, then the best of
+// two timed replays.  Graph replay is how latency-sensitive callers run the
+// library; timing eager launches would measure the host's launch rate instead
+// (about 10 us per call, above the kernel time of every message up to a few
+// hundred KiB per rank).
+hipError_t time_candidate(const void *const *send, void *const *dst, size_t count,
+                          arDataType_t dtype, int nranks, arProtocol_t proto, const arComm *comm,
+                          int threads, uint64_t blocks, int pkt_bytes, int calls, hipStream_t cs,
+                          hipEvent_t e0, hipEvent_t e1, float *us)
+{
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess)
+        return e;
+    hipError_t le = hipSuccess;
+    for (int i = 0; i < calls && le == hipSuccess; ++i)
+        le = launch(send, dst, count, dtype, nranks, proto, comm, threads, blocks, pkt_bytes, 0, cs);
+    e = hipStreamEndCapture(cs, &graph);  // always ends the capture
+    if (le != hipSuccess)
+        e = le;
+    if (e == hipSuccess)
+        e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (e == hipSuccess)
+        e = hipGraphLaunch(exec, cs);
+    float best = 0.0f;
+    for (int rep = 0; rep < 2 && e == hipSuccess; ++rep) {
+        e = hipEventRecord(e0, cs);
+        if (e == hipSuccess)
+            e = hipGraphLaunch(exec, cs);
+        if (e == hipSuccess)
+            e = hipEventRecord(e1, cs);
+        if (e == hipSuccess)
+            e = hipEventSynchronize(e1);
+        float ms = 0.0f;
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&ms, e0, e1);
+        const float t = ms * 1000.0f / (float)calls;
+        if (rep == 0 || t < best)
+            best = t;
+    }
+    if (exec != nullptr)
+        (void)hipGraphExecDestroy(exec);
+    if (graph != nullptr)
+        (void)hipGraphDestroy(graph);
+    *us = best;
+    return e;
+}
+
 // Ranks per simulated node when a hierarchical order is in force, else 0.
 int hierarchy_group(const arComm *comm, int nranks)
 {
@@ -422,12 +472,15 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype, int nranks, size_t maxB
     const size_t stride = (maxBytesPerRank + 255) / 256 * 256;
     char *splane = nullptr, *rplane = nullptr;
     hipEvent_t e0 = nullptr, e1 = nullptr;
-    const hipStream_t st = (hipStream_t)stream;
+    hipStream_t cs = nullptr;  // private stream: graph capture is not allowed on the null stream
     arResult_t result = arSuccess;
-    if (hipMalloc((void **)&splane, stride * (size_t)nranks) != hipSuccess ||
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess ||
+        hipMalloc((void **)&splane, stride * (size_t)nranks) != hipSuccess ||
         hipMalloc((void **)&rplane, stride * (size_t)nranks) != hipSuccess ||
         hipMemset(splane, 0x3c, stride * (size_t)nranks) != hipSuccess ||
-        hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess ||
+        hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
         result = reject(arHipError, "tuning set-up failed");
     }
     std::vector<const void *> send((size_t)nranks);
@@ -473,26 +526,9 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype, int nranks, size_t maxB
                 const int th = c < 0 ? 0 : (proto == arProtoLL ? kLLThreads[c / nb] : kHBThreads[c / nb]);
                 const int bl = c < 0 ? 0 : (proto == arProtoLL ? kLLBlocks[c % nb] : hb_blocks[c % nb]);
                 float us = 0.0f;
-                hipError_t e = hipSuccess;
-                for (int i = 0; i < 2 && e == hipSuccess; ++i)
-                    e = launch(send.data(), dst, count, dtype, nranks,
-                               (arProtocol_t)proto, comm, th, (uint64_t)bl, pkt, 0, st);
-                for (int rep = 0; rep < 2 && e == hipSuccess; ++rep) {
-                    e = hipEventRecord(e0, st);
-                    for (int i = 0; i < calls && e == hipSuccess; ++i)
-                        e = launch(send.data(), dst, count, dtype, nranks,
-                                   (arProtocol_t)proto, comm, th, (uint64_t)bl, pkt, 0, st);
-                    if (e == hipSuccess)
-                        e = hipEventRecord(e1, st);
-                    if (e == hipSuccess)
-                        e = hipEventSynchronize(e1);
-                    float ms = 0.0f;
-                    if (e == hipSuccess)
-                        e = hipEventElapsedTime(&ms, e0, e1);
-                    const float t = ms * 1000.0f / (float)calls;
-                    if (rep == 0 || t < us)
-                        us = t;
-                }
+                const hipError_t e =
+                    time_candidate(send.data(), dst, count, dtype, nranks, (arProtocol_t)proto,
+                                   comm, th, (uint64_t)bl, pkt, calls, cs, e0, e1, &us);
                 if (e != hipSuccess) {
                     result = reject(arHipError, hipGetErrorString(e));
                     break;
@@ -510,6 +546,8 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype, int nranks, size_t maxB
         (void)hipEventDestroy(e1);
     if (hipDeviceSynchronize() != hipSuccess && result == arSuccess)
         result = reject(arHipError, "synchronisation after tuning failed");
+    if (cs != nullptr)
+        (void)hipStreamDestroy(cs);
     (void)hipFree(splane);
     (void)hipFree(rplane);
     if (result == arSuccess) {

@@ -183,9 +183,12 @@ arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
  * arOptHBBlocks (HB) are set; arProtoAuto then picks the faster protocol.
  * Tuning again overwrites the table; sizes never tuned use built-in defaults.
  *
- * Allocates two scratch planes of nranks * maxBytesPerRank bytes for the
- * duration, runs on `stream` and synchronises the device: never call it while
- * a stream is being captured.  Returns arInvalidArgument for a NULL comm or
+ * Each candidate is timed the way latency-sensitive callers run the library:
+ * its calls captured into a HIP graph on a private stream of the tuner, and
+ * the graph replayed (eager launches would time the host's launch rate at
+ * small sizes).  Allocates two scratch planes of nranks * maxBytesPerRank
+ * bytes for the duration, waits for `stream` first and synchronises the
+ * device at the end: never call it while a stream is being captured.  Returns arInvalidArgument for a NULL comm or
  * maxBytesPerRank outside 512 B .. 16 GiB, arUnsupported for a dtype or rank
  * count arAllReduce would reject, arInvalidUsage if the communicator is not on
  * the current device, arHipError if memory or a launch fails, arTimeout if an
