@@ -451,6 +451,7 @@ def main():
                          "per rank (2 KiB-1 MiB), 10 calls per hipGraph; HB two-shot in place "
                          "at 8192x8192 per rank (128 MiB) for the HBM roofline"),
             "nranks": R, "calls_per_graph": CALLS_PER_GRAPH,
+            "element_type": "bf16", "accumulate": "f32 in rank order, one RNE rounding",
             "parallelism": "1 GPU, ranks simulated in HBM",
             "tuned": not args.no_tune,
         },
