@@ -32,7 +32,12 @@
  * SGLang guide describes when a guard fails (sections 4.3 and 5).
  *
  * All entry points are host functions.  A communicator is used from one host
- * thread and one stream at a time, like an NCCL communicator.
+ * thread and one stream at a time, like an NCCL communicator: its LL packet
+ * memory is shared by its calls, so two LL calls of one communicator must not
+ * overlap in time.  Several communicators may run at once on different
+ * streams.  An LL call needs all of its workgroups resident together, so
+ * concurrent kernels that fill the GPU can delay an LL call up to its wait
+ * bound (arOptPollTimeoutUs), after which it records arTimeout.
  */
 #ifndef AR_ALLREDUCE_H
 #define AR_ALLREDUCE_H

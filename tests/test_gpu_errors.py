@@ -65,3 +65,36 @@ def test_option_ranges(comm):
         comm.set_option(ar.arOption.arOptLLThreads, 96)
     comm.set_option(ar.arOption.arOptHBUnroll, 4)
     assert comm.get_option(ar.arOption.arOptHBUnroll) == 4
+
+
+def test_two_communicators_on_two_streams_at_once(orc):
+    """Each communicator has its own packet memory, so LL calls of two of them
+    may overlap in time on two streams."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gpu_util import CODES, PROTO, assert_parity, expect
+    comms = [ar.Comm(device="cuda:0", max_ranks=8, max_ll_bytes_per_rank=1 << 20)
+             for _ in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    R, N = 8, 100_003
+    xs = [inputs.make(R, N, "bf16", "uniform", seed=60 + i) for i in range(2)]
+    planes = []
+    for x in xs:
+        _, sv = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+        _, rv = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+        for r in range(R):
+            sv[r].copy_(x[r])
+        planes.append((sv, rv))
+    torch.cuda.synchronize()
+    note("two communicators, LL on two streams, 20 calls each")
+    for _ in range(20):
+        for c, st, (sv, rv) in zip(comms, streams, planes):
+            rc = ar.arAllReduce([t.data_ptr() for t in sv], [t.data_ptr() for t in rv], N,
+                                CODES["bf16"], ar.arRedOp.arSum, R, PROTO["ll"], c.handle,
+                                st.cuda_stream)
+            assert rc == ar.arResult.arSuccess
+    torch.cuda.synchronize()
+    for c, x, (sv, rv) in zip(comms, xs, planes):
+        assert c.async_error() == ar.arResult.arSuccess
+        assert_parity(torch.stack([t.cpu() for t in rv]), expect(orc, x), "concurrent LL")
+        c.close()

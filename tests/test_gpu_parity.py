@@ -12,7 +12,7 @@ import all_reduce_amd as ar
 import exact_model as em
 import pins
 from all_reduce_amd import inputs
-from gpu_util import assert_parity, bits, expect, from_bits, run_allreduce
+from gpu_util import assert_parity, bits, expect, from_bits, note, run_allreduce
 
 pytestmark = pytest.mark.gpu
 
@@ -204,3 +204,63 @@ def test_ll_tuning_options_keep_bits(comm, orc, opt, values):
             assert_parity(run_allreduce(comm, x, "ll"), want, f"{opt.name}={v}")
     finally:
         comm.set_option(opt, old)
+
+
+@pytest.mark.parametrize("protocol", ["ll", "hb", "auto"])
+def test_count_zero_touches_nothing(comm, protocol):
+    from gpu_util import CODES, PROTO
+    _, sv = ar.rank_buffers(8, 64, torch.bfloat16, "cuda")
+    plane, rv = ar.rank_buffers(8, 64, torch.bfloat16, "cuda")
+    plane.view(torch.uint8).fill_(0xA5)
+    before = plane.clone()
+    rc = ar.arAllReduce([t.data_ptr() for t in sv], [t.data_ptr() for t in rv], 0,
+                        CODES["bf16"], ar.arRedOp.arSum, 8, PROTO[protocol], comm.handle,
+                        torch.cuda.current_stream().cuda_stream)
+    assert rc == ar.arResult.arSuccess
+    torch.cuda.synchronize()
+    assert torch.equal(plane.view(torch.uint8), before.view(torch.uint8))
+
+
+@pytest.mark.parametrize("staged", [0, 1])
+def test_hb_beyond_4_gib_per_rank(comm, orc, staged):
+    """2^31 + 5 bf16 per rank (> 4 GiB, 64-bit offsets, ragged tail), R = 2.
+
+    Integer inputs in [-4, 4] from a seeded CPU generator pattern: every output
+    is checked against the exact sum on the GPU in slices, and ~1M sampled
+    columns (the last 4096 included) against the oracle."""
+    R, N = 2, (1 << 31) + 5
+    note(f"HB R={R} N={N} bf16 > 4 GiB per rank, staged={staged}")
+    g = torch.Generator().manual_seed(77)
+    period = torch.randint(-4, 5, (R, 1 << 20), generator=g, dtype=torch.int8)
+    _, sv = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    _, rv = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    pd = period.to("cuda")
+    step = 1 << 20
+    for r in range(R):  # rank r: its own random period, tiled
+        for a in range(0, N, step):
+            b = min(a + step, N)
+            sv[r][a:b].copy_(pd[r, : b - a])
+    from gpu_util import CODES, PROTO
+    old = comm.get_option(ar.arOption.arOptHBStaged)
+    comm.set_option(ar.arOption.arOptHBStaged, staged)
+    try:
+        rc = ar.arAllReduce([t.data_ptr() for t in sv], [t.data_ptr() for t in rv], N,
+                            CODES["bf16"], ar.arRedOp.arSum, R, PROTO["hb"], comm.handle,
+                            torch.cuda.current_stream().cuda_stream)
+        assert rc == ar.arResult.arSuccess
+        torch.cuda.synchronize()
+    finally:
+        comm.set_option(ar.arOption.arOptHBStaged, old)
+    big = 1 << 28
+    for a in range(0, N, big):
+        b = min(a + big, N)
+        want = sv[0][a:b].float() + sv[1][a:b].float()
+        for r in range(R):
+            assert torch.equal(rv[r][a:b].float(), want), f"rank {r} slice at {a}"
+    idx = torch.cat([torch.randint(0, N, (1 << 20,), generator=g),
+                     torch.arange(N - 4096, N)])
+    xs = torch.stack([t[idx.to("cuda")].cpu() for t in sv])
+    got = torch.stack([t[idx.to("cuda")].cpu() for t in rv])
+    assert_parity(got, expect(orc, xs), "> 4 GiB per rank, sampled")
+    del sv, rv
+    torch.cuda.empty_cache()

@@ -151,3 +151,15 @@ def test_grouped_degenerate_groups_are_the_flat_order(orc, dtype):
     for g in (1, 12):
         same = pins.bits_of(orc.allreduce_grouped(x, dtype, g), dtype)
         pins.assert_same_bits(same[0], flat[0], dtype, f"group {g}")
+
+
+def test_timed_entry_point_computes_the_same(orc):
+    # the CPU-baseline timing wrapper runs the pinned all-reduce unchanged
+    rng = np.random.default_rng(22)
+    xb = pins.random_bits(rng, "bf16", (8, 3001), emin=-8, emax=8)
+    want = orc.allreduce(xb, "bf16")
+    out = np.empty_like(xb)
+    t = orc.allreduce_into(list(xb), list(out), "bf16", nthreads=2, timed=True)
+    assert t >= 0.0
+    pins.assert_same_bits(out[0], want[0], "bf16", "timed entry point")
+    assert np.array_equal(out, want)
