@@ -514,6 +514,14 @@ def run_configs(B, inputs, sweep_rows, result):
             p["us_per_launch"], p["parity"], p.get("oracle_ms_1"), p.get("oracle_ms_T"))
         add("C4 8192x8192 in place", 8, "bf16", p["elems_per_rank"], "hb", "cold",
             p["us_mean_cold"], p["parity"], p.get("oracle_ms_1"), p.get("oracle_ms_T"))
+    # The C5 dtypes and rank counts get the start-up tuning the bench gives
+    # bf16 R = 8 (unless --no-tune): fp16 up to 512 KiB, fp32 up to 112 MiB.
+    if not B.args.no_tune:
+        t0 = time.perf_counter()
+        for R in (16, 32):
+            B.comm.tune(torch.float16, R, 1 << 19)
+            B.comm.tune(torch.float32, R, 4096 * 7168 * 4)
+        log(f"arCommTune fp16 / fp32 at R = 16, 32: {time.perf_counter() - t0:.2f} s")
     # C5a: R = 16 / 32, 2^18 fp16 integers, both protocols, graph-timed
     for R in (16, 32):
         case = inputs.integer_case(R, "fp16")
