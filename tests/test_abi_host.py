@@ -150,3 +150,14 @@ def test_python_helpers():
     assert ar.dtype_code(torch.float32) == ar.arDataType.arFloat32
     with pytest.raises(ar.ArError):
         ar.dtype_code(torch.int32)
+
+
+def test_plain_c_caller_host_side():
+    """The header compiles as C99 and a C program linked to the library gets
+    the host-side answers (no GPU needed)."""
+    from c_abi import build as cbuild
+    exe = cbuild.HERE / "abi_host.bin"
+    if not exe.exists() or exe.stat().st_mtime < ar.LIBRARY.stat().st_mtime:
+        cbuild.build()
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0 and res.stdout.strip() == "ok", res.stdout + res.stderr
