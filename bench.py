@@ -50,6 +50,8 @@ HBM_PEAK_GBPS = 8000.0
 CALLS_PER_GRAPH = 10
 SWEEP = list(range(10, 20))
 EAGER_WARMUP, EAGER_CALLS = 2, 10
+C5B_BYTES = 4096 * 7168 * 4  # bytes per rank of the fp32 4096 x 7168 workload
+C5B_COUNTERS = "hb_twoshot_fp32_r16_r32_112MiB_counters.txt"
 
 
 def log(msg: str):
@@ -62,7 +64,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--only", choices=["all", "sweep", "prefill", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "sweep", "prefill", "copy", "c5b"], default="all",
                     help="run one part (for profiler passes)")
     ap.add_argument("--configs", action="store_true",
                     help="also measure every named workload and print the full table")
@@ -397,6 +399,29 @@ def main():
                                       "gbps": round(2 * (1 << 30) / (us * 1e-6) / 1e9, 1)}
         del src, dst
 
+    # ---- C5b alone: fp32 R = 16 / 32 at 112 MiB per rank (for profiler passes)
+    if args.only == "c5b":
+        if not args.no_tune:
+            for R in (16, 32):
+                B.comm.tune(torch.float32, R, C5B_BYTES)
+        rows = []
+        for R in (16, 32):
+            case = inputs.integer_case(R, "fp32")
+            x = inputs.make(**case)
+            n = case["count"]
+            sv, rv = B.planes(x)
+            B.launch(sv, rv, n, "hb")
+            torch.cuda.synchronize()
+            g = torch.Generator().manual_seed(99)
+            par = B.parity(x, rv, sample=torch.randint(0, n, (1 << 20,), generator=g))
+            del x
+            us = B.back_to_back_us(sv, rv, n, "hb", args.steps)
+            rows.append({"nranks": R, "parity": par, "us_per_launch": round(us, 2),
+                         "gbps": gbps(R, n, 4, us)})
+            log(f"C5b R={R}: {us:.1f} us per launch, {gbps(R, n, 4, us):.0f} GB/s")
+            del sv, rv
+        result["c5b_hb"] = rows
+
     # ---- every named workload as one table ----------------------------------
     if args.configs and args.only == "all":
         result["configs"] = run_configs(B, inputs, sweep_rows, result)
@@ -468,13 +493,21 @@ def run_configs(B, inputs, sweep_rows, result):
     T = B.threads
     rows = []
 
+    # HBM bytes per launch measured by rocprofv3 for the HBM-bound rows (fused
+    # HB at full size), from the committed counter summaries
+    counted = {("C4 8192x8192 in place", "hb"): _counter_traffic(),
+               ("C5b R=16", "hb"): _counter_traffic(C5B_COUNTERS, "hbm_bytes_per_launch_r16"),
+               ("C5b R=32", "hb"): _counter_traffic(C5B_COUNTERS, "hbm_bytes_per_launch_r32")}
+
     def add(name, R, dtype, n, proto, mode, us, parity, o1=None, oT=None):
         es = 4 if dtype == "fp32" else 2
         g = gbps(R, n, es, us)
+        hbm = counted.get((name, proto)) if mode in ("back-to-back", "cold") else None
         rows.append({"config": name, "R": R, "dtype": dtype, "elems_per_rank": n,
                      "bytes_per_rank": n * es, "proto": proto, "mode": mode,
                      "us_per_call": round(us, 2), "gbps": g,
                      "pct_of_peak": round(100 * g / HBM_PEAK_GBPS, 2),
+                     "counter_gbps": round(hbm / (us * 1e3), 1) if hbm else None,
                      "oracle_ms_1": o1, "oracle_ms_T": oT, "parity": parity})
 
     # C1: R=8, 1024 bf16, eager calls of each protocol
@@ -520,7 +553,7 @@ def run_configs(B, inputs, sweep_rows, result):
         t0 = time.perf_counter()
         for R in (16, 32):
             B.comm.tune(torch.float16, R, 1 << 19)
-            B.comm.tune(torch.float32, R, 4096 * 7168 * 4)
+            B.comm.tune(torch.float32, R, C5B_BYTES)
         log(f"arCommTune fp16 / fp32 at R = 16, 32: {time.perf_counter() - t0:.2f} s")
     # C5a: R = 16 / 32, 2^18 fp16 integers, both protocols, graph-timed
     for R in (16, 32):
@@ -627,13 +660,14 @@ def run_configs(B, inputs, sweep_rows, result):
         B.comm.set_option(O.arOptHBStaged, 0)
 
     log("\n| config | R | dtype | elems/rank | bytes/rank | proto | mode | µs/call | eff. GB/s | "
-        "% of 8 TB/s | oracle ms (1 thr) | oracle ms (T thr) | parity |")
-    log("|---|---:|---|---:|---:|---|---|---:|---:|---:|---:|---:|:---:|")
+        "% of 8 TB/s | counter GB/s | oracle ms (1 thr) | oracle ms (T thr) | parity |")
+    log("|---|---:|---|---:|---:|---|---|---:|---:|---:|---:|---:|---:|:---:|")
     for r in rows:
+        cg = "—" if r["counter_gbps"] is None else f"{r['counter_gbps']:.0f}"
         log(f"| {r['config']} | {r['R']} | {r['dtype']} | {r['elems_per_rank']} | "
             f"{r['bytes_per_rank']} | {r['proto']} | {r['mode']} | {r['us_per_call']:.2f} | "
-            f"{r['gbps']:.0f} | {r['pct_of_peak']:.1f} | {r['oracle_ms_1']} | {r['oracle_ms_T']} | "
-            f"{r['parity']} |")
+            f"{r['gbps']:.0f} | {r['pct_of_peak']:.1f} | {cg} | {r['oracle_ms_1']} | "
+            f"{r['oracle_ms_T']} | {r['parity']} |")
     log(f"(T = {T} host threads)")
     return rows
 
@@ -653,22 +687,24 @@ def _sources_digest() -> str:
     return h.hexdigest()
 
 
-def _counter_traffic():
-    """HBM bytes per launch of the prefill HB kernel from the committed counter
-    summary, or None when that summary was taken from other kernel sources."""
+def _counter_traffic(summary="hb_twoshot_bf16_r8_128MiB_counters.txt",
+                     key="hbm_bytes_per_launch"):
+    """HBM bytes per launch of an HB kernel from a committed counter summary
+    under profiles/, or None when that summary is missing or was taken from
+    other kernel sources."""
     from pathlib import Path
-    path = Path(__file__).resolve().parent / "profiles" / "hb_twoshot_bf16_r8_128MiB_counters.txt"
+    path = Path(__file__).resolve().parent / "profiles" / summary
     if not path.exists():
         return None
     fields = {}
     for line in path.read_text().splitlines():
         if ":" in line and not line.startswith(("#", " ")):
-            key, _, val = line.partition(":")
-            fields[key.strip()] = val.strip()
+            k, _, val = line.partition(":")
+            fields[k.strip()] = val.strip()
     if fields.get("source_sha256") != _sources_digest():
         return None
     try:
-        return int(fields["hbm_bytes_per_launch"])
+        return int(fields[key])
     except (KeyError, ValueError):
         return None
 
