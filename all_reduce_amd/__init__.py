@@ -288,8 +288,11 @@ class Comm:
             raise ArError(r, "arCommGetAsyncError")
         return arResult(e)
 
-    def all_reduce(self, send, recv=None, protocol="hb", stream=None):
-        """Sum all-reduce of the tensors in ``send`` into ``recv`` (default: in place)."""
+    def all_reduce(self, send, recv=None, protocol="auto", stream=None):
+        """Sum all-reduce of the tensors in ``send`` into ``recv`` (default: in place).
+
+        ``protocol`` is "ll", "hb" or "auto" (the tuned faster one; HB where
+        nothing was tuned)."""
         if recv is None:
             recv = send
         if len(send) != len(recv) or not send:

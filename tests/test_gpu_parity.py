@@ -264,3 +264,33 @@ def test_hb_beyond_4_gib_per_rank(comm, orc, staged):
     assert_parity(got, expect(orc, xs), "> 4 GiB per rank, sampled")
     del sv, rv
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("protocol", ["ll", "hb", "auto"])
+def test_comm_all_reduce_convenience(comm, orc, protocol):
+    x = inputs.make(8, 10_007, "bf16", "normal", seed=2024)
+    want = expect(orc, x)
+    send = [t.to("cuda") for t in x]
+    recv = [torch.empty_like(t) for t in send]
+    note(f"Comm.all_reduce {protocol}")
+    out = comm.all_reduce(send, recv, protocol=protocol)
+    torch.cuda.synchronize()
+    assert_parity(torch.stack([t.cpu() for t in out]), want, f"all_reduce {protocol}")
+    comm.all_reduce(send, protocol=protocol)  # in place
+    torch.cuda.synchronize()
+    assert_parity(torch.stack([t.cpu() for t in send]), want, f"all_reduce {protocol} in place")
+
+
+def test_comm_all_reduce_rejects_bad_tensors(comm):
+    a = [torch.zeros(64, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    with pytest.raises(ValueError):
+        comm.all_reduce([a[0], a[1].to(torch.float16)])
+    with pytest.raises(ValueError):
+        comm.all_reduce(a, [a[0]])
+    with pytest.raises(ValueError):
+        comm.all_reduce([a[0], torch.zeros(128, dtype=torch.bfloat16, device="cuda")[::2]])
+    with pytest.raises(ValueError):
+        comm.all_reduce([a[0], torch.zeros(64, dtype=torch.bfloat16)])
+    with pytest.raises(ar.ArError):  # 16-bit x 3 = 6 bytes apart: not 16-byte aligned
+        base = torch.zeros(256, dtype=torch.bfloat16, device="cuda")
+        comm.all_reduce([base[0:64], base[3:67]], [base[128:192], base[192:256]])
