@@ -508,7 +508,9 @@ def run_configs(B, inputs, sweep_rows, result):
                      "us_per_call": round(us, 2), "gbps": g,
                      "pct_of_peak": round(100 * g / HBM_PEAK_GBPS, 2),
                      "counter_gbps": round(hbm / (us * 1e3), 1) if hbm else None,
-                     "oracle_ms_1": o1, "oracle_ms_T": oT, "parity": parity})
+                     "oracle_ms_1": o1, "oracle_ms_T": oT,
+                     "oracle_gbps_T": round(2 * R * n * es / (oT * 1e6), 2) if oT else None,
+                     "parity": parity})
 
     # C1: R=8, 1024 bf16, eager calls of each protocol
     case = inputs.WORKLOADS["C1"]
@@ -660,14 +662,15 @@ def run_configs(B, inputs, sweep_rows, result):
         B.comm.set_option(O.arOptHBStaged, 0)
 
     log("\n| config | R | dtype | elems/rank | bytes/rank | proto | mode | µs/call | eff. GB/s | "
-        "% of 8 TB/s | counter GB/s | oracle ms (1 thr) | oracle ms (T thr) | parity |")
-    log("|---|---:|---|---:|---:|---|---|---:|---:|---:|---:|---:|---:|:---:|")
+        "% of 8 TB/s | counter GB/s | oracle ms (1 thr) | oracle ms (T thr) | oracle GB/s (T thr) | "
+        "parity |")
+    log("|---|---:|---|---:|---:|---|---|---:|---:|---:|---:|---:|---:|---:|:---:|")
     for r in rows:
         cg = "—" if r["counter_gbps"] is None else f"{r['counter_gbps']:.0f}"
         log(f"| {r['config']} | {r['R']} | {r['dtype']} | {r['elems_per_rank']} | "
             f"{r['bytes_per_rank']} | {r['proto']} | {r['mode']} | {r['us_per_call']:.2f} | "
             f"{r['gbps']:.0f} | {r['pct_of_peak']:.1f} | {cg} | {r['oracle_ms_1']} | "
-            f"{r['oracle_ms_T']} | {r['parity']} |")
+            f"{r['oracle_ms_T']} | {r['oracle_gbps_T']} | {r['parity']} |")
     log(f"(T = {T} host threads)")
     return rows
 
