@@ -242,7 +242,7 @@ def gbps(R, n, esize, us):
 def main():
     args = parse()
     if args.gpus != 1:
-        log(f"bench.py: --gpus {args.gpus} is not supported. This build runs on one GPU: "
+        log(f"bench.py: --gpus {args.gpus} is not supported. This library runs on one GPU: "
             "the R ranks are simulated as R buffers in one GPU's HBM, so there is no "
             "multi-GPU run to launch.")
         return 2
