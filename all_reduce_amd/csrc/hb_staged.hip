@@ -6,7 +6,7 @@
 // ("SGLang 中的 MSCCL++ All-Reduce 基准测试与推理集成指南", blog.gitcode.com,
 // section 4.4, rsag) are separated by a synchronisation: GPU c reduces chunk
 // c into its own buffer, signals, and the peers then fetch the reduced chunk
-// -- the "few syncs" of the HB protocol ("MSCCL++：让 GPU 通信像 CUDA 一样可编程",
+// -- the HB protocol's rare synchronisation ("MSCCL++：让 GPU 通信像 CUDA 一样可编程",
 // infinitensor.com/news/50, "MemoryChannel").  This file runs that staged
 // form on one GPU, to measure what the stage boundary costs:
 //   stage 1  for every position of chunk c: load the R inputs, reduce in

@@ -128,7 +128,7 @@ typedef enum {
     /* HB: 1 = the staged two-shot, an ablation of the fused default: the
      * reduce-scatter writes each reduced chunk to its owner rank's output
      * only, a kernel boundary stands for the synchronisation between the
-     * shots (the "few syncs" of the HB protocol, "MSCCL++：让 GPU 通信像 CUDA
+     * shots (the HB protocol synchronises rarely, "MSCCL++：让 GPU 通信像 CUDA
      * 一样可编程", "MemoryChannel"), and the all-gather copies each chunk from
      * its owner to the other outputs.  Same result bits; 2 * bytes per rank
      * more traffic and one more launch.  Launch shape from arOptHBThreads /
