@@ -66,6 +66,12 @@ MUTANTS = {
                                        "    for (int g = nranks / group - 1; g >= 0; --g) {"),
     "grouped drops the last group": ("    for (int g = 0; g < nranks / group; ++g) {",
                                      "    for (int g = 0; g < nranks / group - 1; ++g) {"),
+    "grouped reverses ranks in a node": ("            const int j = g * group + l;",
+                                         "            const int j = g * group + (group - 1 - l);"),
+    "grouped nodes strided, not consecutive": ("            const int j = g * group + l;",
+                                               "            const int j = l * (nranks / group) + g;"),
+    "grouped total from +0": ("        total = (g == 0) ? part : total + part;",
+                              "        total = total + part;"),
 }
 
 
