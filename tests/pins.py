@@ -388,20 +388,26 @@ def pin_widen_fp16(orc):
 GOLDEN_GROUPED = Path(__file__).resolve().parent / "golden" / "hand_cases_grouped.txt"
 
 
-def pin_grouped_hand_cases(orc):
-    n = 0
+def load_grouped_hand_cases():
+    """(dtype, group, [rank input bits], output bits) from the grouped fixture."""
+    cases = []
     for line in GOLDEN_GROUPED.read_text().splitlines():
         line = line.split("#", 1)[0].strip()
         if not line:
             continue
         dtype, group, ins, out = [t.strip() for t in line.split("|")]
-        cols = [[int(t, 16) for t in ins.split()]]
-        got = orc.allreduce_grouped(to_array(cols, dtype), dtype, int(group))
-        for r in range(len(cols[0])):
-            assert_same_bits(got[r], np.array([int(out, 16)]), dtype,
-                             f"grouped hand case {dtype} g={group} {ins}")
-        n += 1
-    assert n >= 5, "grouped hand-case fixture went missing"
+        cases.append((dtype, int(group), [int(t, 16) for t in ins.split()], int(out, 16)))
+    return cases
+
+
+def pin_grouped_hand_cases(orc):
+    cases = load_grouped_hand_cases()
+    for dtype, group, ins, out in cases:
+        got = orc.allreduce_grouped(to_array([ins], dtype), dtype, group)
+        for r in range(len(ins)):
+            assert_same_bits(got[r], np.array([out]), dtype,
+                             f"grouped hand case {dtype} g={group} {[hex(v) for v in ins]}")
+    assert len(cases) >= 5, "grouped hand-case fixture went missing"
 
 
 @functools.lru_cache(maxsize=None)

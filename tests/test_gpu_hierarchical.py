@@ -123,3 +123,15 @@ def test_grouping_rules(comm):
     torch.cuda.synchronize()
     with pytest.raises(ar.ArError):
         comm.set_option(ar.arOption.arOptHBGroup, 33)
+
+
+def test_grouped_hand_cases(comm):
+    """The hand-derived grouped cases, through the C ABI on the HB kernel."""
+    for dtype, group, ins, out in pins.load_grouped_hand_cases():
+        x = from_bits(pins.to_array([ins], dtype).view(
+            np.uint32 if dtype == "fp32" else np.uint16), dtype)
+        with grouped(comm, group):
+            got = bits(run_allreduce(comm, x, "hb"))
+        for r in range(len(ins)):
+            pins.assert_same_bits(got[r], np.array([out]), dtype,
+                                  f"grouped hand case {dtype} g={group} {[hex(v) for v in ins]}")
