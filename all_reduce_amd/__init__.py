@@ -162,12 +162,21 @@ def arCommGetTunedShape(comm, dtype: int, nranks: int, protocol: int, bytes_per_
     return r, shape
 
 
+def _pointer_array(ptrs: Sequence[int] | None, nranks: int):
+    """ctypes array of device pointers, NULL-padded to ``nranks`` entries so the
+    library never reads past it (it rejects nranks > AR_MAX_RANKS before reading
+    any pointer, and reports a NULL entry as arInvalidArgument)."""
+    if ptrs is None:
+        return None
+    n = max(1, len(ptrs), min(max(int(nranks), 0), AR_MAX_RANKS))
+    return (ctypes.c_void_p * n)(*ptrs)
+
+
 def arAllReduce(sendbufs: Sequence[int] | None, recvbufs: Sequence[int] | None, count: int,
                 dtype: int, op: int, nranks: int, protocol: int, comm, stream) -> int:
     """Device pointers as integers; ``None`` passes a NULL array."""
-    vp = ctypes.c_void_p
-    s = None if sendbufs is None else (vp * max(1, len(sendbufs)))(*sendbufs)
-    d = None if recvbufs is None else (vp * max(1, len(recvbufs)))(*recvbufs)
+    s = _pointer_array(sendbufs, nranks)
+    d = _pointer_array(recvbufs, nranks)
     return library().arAllReduce(s, d, count, int(dtype), int(op), nranks, int(protocol),
                                  comm, stream)
 

@@ -75,6 +75,8 @@ CASES = [
     ("sends may overlap", dict(send=[A, A], recv=[A + 4 * L, A + 5 * L]), "arInvalidArgument",
      "NULL comm"),
     ("count zero", dict(count=0, send=None, recv=None), "arSuccess", None),
+    # fewer pointers than ranks: the binding pads with NULL, the library rejects
+    ("short pointer list", dict(nranks=4), "arInvalidArgument", "NULL rank buffer"),
 ]
 
 CHILD = r"""
