@@ -234,7 +234,9 @@ class Comm:
         self.max_ll_bytes_per_rank = max_ll_bytes_per_rank
 
     def close(self):
+        """Free the communicator after the device has finished the work using it."""
         if self.handle is not None:
+            _torch().cuda.synchronize(self.device)
             r = arCommDestroy(self.handle)
             self.handle = None
             if r != 0:
