@@ -24,17 +24,25 @@ Default run (inputs resident in HBM before every timed region):
   cache).  Also reported ("cold"): ``--warmup`` + ``--steps`` calls each inside
   its own event pair, with the inputs restored from a pristine copy and 512 MiB
   written to flush the last-level cache before each (untimed).
+* graph_floor_us -- the per-call cost of a graph-replayed one-rank, 16-byte
+  call (one workgroup), to split LL latency into launch floor and protocol.
 * cpu_baseline -- the CPU oracle (plain C, OpenMP) timed on this host on the
-  same LL sweep inputs, a bounded sample.
+  same LL sweep inputs, a bounded sample (1.5 s of calls per size).
 
 ``value`` is the mean LL latency per call over the sweep in microseconds
 (lower is better).  Every timed configuration is first checked bit for bit
 against the oracle.
 
 ``--configs`` adds every named workload (R = 8 small, the sweep, decode,
-prefill, and R = 16 / 32 with integer data in fp16 and fp32) as rows of one
-table: µs per call, effective GB/s (2 * R * bytes per rank / time), share of
-the 8 TB/s HBM peak, the oracle's time at 1 and at all host threads, parity.
+prefill, and R = 16 / 32 with integer data in fp16 and fp32, tuned like the
+default run) as rows of one table, plus the hierarchical order (nodes of 8) and
+the staged HB form at their shapes: µs per call, effective GB/s (2 * R * bytes
+per rank / time), share of the 8 TB/s HBM peak, HBM GB/s from the committed
+rocprofv3 counter summaries where one covers the kernel, the oracle's time at
+1 and at all host threads and its own GB/s, parity.
+
+``--only {sweep, prefill, copy, c5b}`` runs one part alone (for profiler
+passes; c5b is the fp32 R = 16 / 32 workload at 112 MiB per rank).
 """
 from __future__ import annotations
 
