@@ -131,11 +131,11 @@ __global__ __launch_bounds__(hb_max_threads(RMAX)) void hb_twoshot(HBParams<RMAX
                         if (EXACT || j < (int)n) {
                             float x[T::kPerWord];
                             T::widen(v[u][j][q], x);
-                            if (kGrouped && j % node == 0) {
+                            if (kGrouped && (uint32_t)j % node == 0) {
                                 // a node is complete: fold its partial in
 #pragma unroll
                                 for (int e = 0; e < T::kPerWord; ++e) {
-                                    total[e] = j == node ? acc[e] : total[e] + acc[e];
+                                    total[e] = (uint32_t)j == node ? acc[e] : total[e] + acc[e];
                                     acc[e] = x[e];
                                 }
                             } else {
