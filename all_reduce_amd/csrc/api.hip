@@ -40,6 +40,19 @@ arResult_t reject(arResult_t r, const char *why)
     return r;
 }
 
+// The integer a caller passed for an enum argument.  A C caller may pass any
+// int, and reading a value outside the enumerators' range as the C++ enum type
+// is undefined, so entry points read enum arguments as int, validate them, and
+// convert back only values known to be valid.
+template <typename E>
+int raw(const E &e)
+{
+    static_assert(sizeof(E) == sizeof(int), "the ABI's enums are int-sized");
+    int v;
+    memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 size_t elem_bytes(arDataType_t dtype)
 {
     return dtype == arFloat32 ? 4 : 2;
@@ -67,7 +80,7 @@ constexpr int64_t kDefaults[kOptionCount] = {
 
 // Argument checks shared by every protocol.  No HIP call.
 arResult_t validate(const void *const *sendbufs, void *const *recvbufs, size_t count,
-                    arDataType_t dtype, arRedOp_t op, int nranks, arProtocol_t protocol)
+                    int dtype, int op, int nranks, int protocol)
 {
     if (dtype != arBfloat16 && dtype != arFloat16 && dtype != arFloat32)
         return reject(arUnsupported, "dtype must be bf16, fp16 or fp32");
@@ -83,7 +96,7 @@ arResult_t validate(const void *const *sendbufs, void *const *recvbufs, size_t c
         return reject(arInvalidArgument, "count too large");
     if (sendbufs == nullptr || recvbufs == nullptr)
         return reject(arInvalidArgument, "NULL buffer array");
-    const size_t len = count * elem_bytes(dtype);
+    const size_t len = count * elem_bytes((arDataType_t)dtype);
     for (int r = 0; r < nranks; ++r) {
         const uintptr_t s = (uintptr_t)sendbufs[r], d = (uintptr_t)recvbufs[r];
         if (s == 0 || d == 0)
@@ -230,7 +243,7 @@ extern "C" {
 
 const char *arGetErrorString(arResult_t result)
 {
-    switch (result) {
+    switch (raw(result)) {
     case arSuccess: return "arSuccess: no error";
     case arInvalidArgument: return "arInvalidArgument: invalid argument";
     case arUnsupported: return "arUnsupported: request not supported, use another all-reduce";
@@ -346,10 +359,11 @@ arResult_t arCommGetAsyncError(arComm_t comm, arResult_t *asyncError)
     return arSuccess;
 }
 
-arResult_t arCommSetOption(arComm_t comm, arOption_t option, int64_t value)
+arResult_t arCommSetOption(arComm_t comm, arOption_t option_arg, int64_t value)
 {
     if (comm == nullptr)
         return reject(arInvalidArgument, "NULL comm");
+    const int option = raw(option_arg);
     bool ok = false;
     switch (option) {
     case arOptPollTimeoutUs: ok = value >= 1 && value <= 600000000; break;
@@ -379,23 +393,27 @@ arResult_t arCommSetOption(arComm_t comm, arOption_t option, int64_t value)
     return arSuccess;
 }
 
-arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value)
+arResult_t arCommGetOption(arComm_t comm, arOption_t option_arg, int64_t *value)
 {
     if (comm == nullptr || value == nullptr)
         return reject(arInvalidArgument, "NULL argument");
-    if ((int)option < 0 || (int)option >= kOptionCount)
+    const int option = raw(option_arg);
+    if (option < 0 || option >= kOptionCount)
         return reject(arInvalidArgument, "unknown option");
     *value = comm->opt[option];
     return arSuccess;
 }
 
 arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_t count,
-                       arDataType_t dtype, arRedOp_t op, int nranks, arProtocol_t protocol,
-                       arComm_t comm, arStream_t stream)
+                       arDataType_t dtype_arg, arRedOp_t op_arg, int nranks,
+                       arProtocol_t protocol_arg, arComm_t comm, arStream_t stream)
 {
-    arResult_t r = validate(sendbufs, recvbufs, count, dtype, op, nranks, protocol);
+    arResult_t r = validate(sendbufs, recvbufs, count, raw(dtype_arg), raw(op_arg), nranks,
+                            raw(protocol_arg));
     if (r != arSuccess || count == 0)
         return r;
+    const arDataType_t dtype = (arDataType_t)raw(dtype_arg);
+    const arProtocol_t protocol = (arProtocol_t)raw(protocol_arg);
     if (comm == nullptr)
         return reject(arInvalidArgument, "NULL comm");
     const size_t bytes = count * elem_bytes(dtype);
@@ -453,13 +471,15 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
     return arSuccess;
 }
 
-arResult_t arCommTune(arComm_t comm, arDataType_t dtype, int nranks, size_t maxBytesPerRank,
-                      arStream_t stream)
+arResult_t arCommTune(arComm_t comm, arDataType_t dtype_arg, int nranks,
+                      size_t maxBytesPerRank, arStream_t stream)
 {
     if (comm == nullptr)
         return reject(arInvalidArgument, "NULL comm");
-    if (dtype != arBfloat16 && dtype != arFloat16 && dtype != arFloat32)
+    const int dti = raw(dtype_arg);
+    if (dti != arBfloat16 && dti != arFloat16 && dti != arFloat32)
         return reject(arUnsupported, "dtype must be bf16, fp16 or fp32");
+    const arDataType_t dtype = (arDataType_t)dti;
     if (nranks < 1 || nranks > AR_MAX_RANKS)
         return reject(arUnsupported, "nranks must be in 1..32");
     if (maxBytesPerRank < 512 || maxBytesPerRank > ((size_t)1 << 34))
@@ -560,12 +580,13 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype, int nranks, size_t maxB
     return result;
 }
 
-arResult_t arCommGetTunedShape(arComm_t comm, arDataType_t dtype, int nranks,
-                               arProtocol_t protocol, size_t bytesPerRank, int inPlace,
+arResult_t arCommGetTunedShape(arComm_t comm, arDataType_t dtype_arg, int nranks,
+                               arProtocol_t protocol_arg, size_t bytesPerRank, int inPlace,
                                arTunedShape_t *shape)
 {
     if (comm == nullptr || shape == nullptr)
         return reject(arInvalidArgument, "NULL argument");
+    const int dtype = raw(dtype_arg), protocol = raw(protocol_arg);
     if ((dtype != arBfloat16 && dtype != arFloat16 && dtype != arFloat32) || nranks < 1 ||
         nranks > AR_MAX_RANKS || (protocol != arProtoLL && protocol != arProtoHB) ||
         bytesPerRank == 0 || (inPlace != 0 && inPlace != 1))
