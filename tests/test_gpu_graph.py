@@ -79,3 +79,49 @@ def test_graph_alternating_inputs(comm, orc, protocol, N):
         from gpu_util import run_allreduce
         assert_parity(run_allreduce(comm, x_small, protocol), expect(orc, x_small), "eager")
     assert comm.async_error() == ar.arResult.arSuccess
+
+
+@pytest.mark.parametrize("protocol,pkt", [("ll", 8), ("ll", 16), ("hb", 0)])
+@pytest.mark.parametrize("N", [1024 + 3, 65536 + 5, 1 << 19])
+def test_stress_thousands_of_replayed_calls(comm, orc, protocol, pkt, N):
+    """50 calls alternating two inputs in one graph, replayed 40 times (2000
+    calls): every replay's outputs and the error word are checked, so a packet
+    left stale by any call would show up in the next one."""
+    R, dt = 8, "bf16"
+    xa = inputs.make(R, N, dt, "uniform", seed=141)
+    xb = inputs.make(R, N, dt, "normal", seed=142)
+    want_a, want_b = expect(orc, xa), expect(orc, xb)
+    _, sa = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    _, sb = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    _, da = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    _, db = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    for r in range(R):
+        sa[r].copy_(xa[r])
+        sb[r].copy_(xb[r])
+    old = comm.get_option(ar.arOption.arOptLLPacketBytes)
+    comm.set_option(ar.arOption.arOptLLPacketBytes, pkt)
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call(comm, sa, da, N, dt, protocol)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(50):
+                call(comm, sa if i % 2 == 0 else sb, da if i % 2 == 0 else db, N, dt, protocol)
+        torch.cuda.synchronize()
+        note(f"stress {protocol}/{pkt} N={N}: 40 replays of 50 calls")
+        for rep in range(40):
+            g.replay()
+            if rep % 10 == 9:
+                torch.cuda.synchronize()
+                assert comm.async_error() == ar.arResult.arSuccess, f"replay {rep}"
+                assert_parity(torch.stack([t.cpu() for t in da]), want_a, f"A after {rep}")
+                assert_parity(torch.stack([t.cpu() for t in db]), want_b, f"B after {rep}")
+        torch.cuda.synchronize()
+        del g
+    finally:
+        comm.set_option(ar.arOption.arOptLLPacketBytes, old)
+    assert comm.async_error() == ar.arResult.arSuccess
