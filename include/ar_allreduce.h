@@ -13,11 +13,12 @@
  * ncclAllReduce), with the R rank pointers of the simulated group passed as
  * arrays.  Two protocols from the page's MemoryChannel table are offered:
  *
- *   arProtoLL  low latency: one kernel, flag-carrying 8-byte packets, polled
- *              per wavefront; meant for decode-size messages.
+ *   arProtoLL  low latency: one kernel, flag-carrying 8-byte (or 16-byte)
+ *              packets, polled per wavefront; meant for decode-size messages.
  *   arProtoHB  high bandwidth: two-shot reduce-scatter by chunk then
  *              all-gather, 128-bit bulk loads and stores, no flags; meant for
- *              prefill-size messages.
+ *              prefill-size messages.  A staged form with a kernel boundary
+ *              between the shots is available as an option.
  *
  * Both give the same result: for every element i,
  *     a = x_0[i];  a = a + x_j[i] for j = 1..R-1 (binary32, in this order);
@@ -193,8 +194,9 @@ arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
  * the graph replayed (eager launches would time the host's launch rate at
  * small sizes).  Allocates two scratch planes of nranks * maxBytesPerRank
  * bytes for the duration, waits for `stream` first and synchronises the
- * device at the end: never call it while a stream is being captured.  Returns arInvalidArgument for a NULL comm or
- * maxBytesPerRank outside 512 B .. 16 GiB, arUnsupported for a dtype or rank
+ * device at the end: never call it while a stream is being captured.
+ * Returns arInvalidArgument for a NULL comm or maxBytesPerRank outside
+ * 512 B .. 16 GiB, arUnsupported for a dtype or rank
  * count arAllReduce would reject, arInvalidUsage if the communicator is not on
  * the current device, arHipError if memory or a launch fails, arTimeout if an
  * LL wait ran out during tuning (then reset the communicator). */
@@ -240,7 +242,9 @@ arResult_t arCommGetTunedShape(arComm_t comm, arDataType_t dtype, int nranks,
  * send buffers may overlap one another (they are only read).
  * LL also needs nranks <= the communicator's maxRanks and count * element
  * size <= its maxLLBytesPerRank (arInvalidUsage otherwise); arProtoAuto only
- * picks LL where it can run.
+ * picks LL where it can run.  With a hierarchical order set (arOptHBGroup),
+ * nranks must be a multiple of the group (arInvalidUsage otherwise), LL and
+ * the staged HB form return arUnsupported, and arProtoAuto runs HB.
  *
  * The call only enqueues work and returns; the buffers belong to the caller
  * and must stay valid until the work has run (for a captured graph, as long
