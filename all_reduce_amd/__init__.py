@@ -58,6 +58,8 @@ class arOption(IntEnum):
     arOptHBGroup = 9
     arOptLLPacketBytes = 10
     arOptHBStaged = 11
+    arOptLLFlagScheme = 12
+    arOptDebugSeqStart = 13
 
 
 AR_MAX_RANKS = 32

@@ -76,6 +76,8 @@ constexpr int64_t kDefaults[kOptionCount] = {
     0,        // arOptHBGroup (flat order)
     0,        // arOptLLPacketBytes (tuned, else 8)
     0,        // arOptHBStaged (fused)
+    0,        // arOptLLFlagScheme (cleared)
+    0,        // arOptDebugSeqStart
 };
 
 // Argument checks shared by every protocol.  No HIP call.
@@ -154,11 +156,11 @@ arProtocol_t resolve_protocol(const arComm *comm, arDataType_t dtype, int nranks
 
 hipError_t launch(const void *const *send, void *const *recv, size_t count, arDataType_t dtype,
                   int nranks, arProtocol_t proto, const arComm *comm, int threads,
-                  uint64_t blocks, int pkt_bytes, int group, hipStream_t stream)
+                  uint64_t blocks, int pkt_bytes, int scheme, int group, hipStream_t stream)
 {
     return proto == arProtoLL
                ? ar::launch_ll(send, recv, count, (int)dtype, nranks, comm, threads, blocks,
-                               pkt_bytes, stream)
+                               pkt_bytes, scheme, stream)
                : ar::launch_hb(send, recv, count, (int)dtype, nranks, comm, threads, blocks, group,
                                stream);
 }
@@ -171,8 +173,8 @@ hipError_t launch(const void *const *send, void *const *recv, size_t count, arDa
 // hundred KiB per rank).
 hipError_t time_candidate(const void *const *send, void *const *dst, size_t count,
                           arDataType_t dtype, int nranks, arProtocol_t proto, const arComm *comm,
-                          int threads, uint64_t blocks, int pkt_bytes, int calls, hipStream_t cs,
-                          hipEvent_t e0, hipEvent_t e1, float *us)
+                          int threads, uint64_t blocks, int pkt_bytes, int scheme, int calls,
+                          hipStream_t cs, hipEvent_t e0, hipEvent_t e1, float *us)
 {
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
@@ -181,7 +183,8 @@ hipError_t time_candidate(const void *const *send, void *const *dst, size_t coun
         return e;
     hipError_t le = hipSuccess;
     for (int i = 0; i < calls && le == hipSuccess; ++i)
-        le = launch(send, dst, count, dtype, nranks, proto, comm, threads, blocks, pkt_bytes, 0, cs);
+        le = launch(send, dst, count, dtype, nranks, proto, comm, threads, blocks, pkt_bytes, scheme,
+                    0, cs);
     e = hipStreamEndCapture(cs, &graph);  // always ends the capture
     if (le != hipSuccess)
         e = le;
@@ -293,24 +296,32 @@ arResult_t arCommCreate(arComm_t *comm, int device, int maxRanks, size_t maxLLBy
     c->wall_clock_khz = (uint64_t)clock_khz;
 
     // Packets: 8 bytes for each 4 payload bytes; round each rank's region up
-    // to a whole number of 256-byte lines.
+    // to a whole number of 512-byte groups (the sequenced scheme's unit), with
+    // one 4-byte sequence entry per group and rank region.
     const uint64_t words = (maxLLBytesPerRank + 3) / 4;
-    c->pkt_stride = (words + 31) / 32 * 32;
+    c->pkt_stride = (words + 63) / 64 * 64;
     const size_t pkt_bytes = (size_t)maxRanks * c->pkt_stride * sizeof(uint64_t);
+    c->seq_words = c->pkt_stride / 64 * (uint64_t)maxRanks;
+    const size_t seq_bytes = c->seq_words * sizeof(uint32_t);
     c->ll16_ok = pkt_bytes < ((size_t)1 << 32);
     if (hipMalloc((void **)&c->ctrl, 256) != hipSuccess) {
         delete c;
         return reject(arHipError, "hipMalloc of control words failed");
     }
     c->pkts = nullptr;
-    if (pkt_bytes > 0 && hipMalloc((void **)&c->pkts, pkt_bytes) != hipSuccess) {
+    c->seq = nullptr;
+    if ((pkt_bytes > 0 && hipMalloc((void **)&c->pkts, pkt_bytes) != hipSuccess) ||
+        (seq_bytes > 0 && hipMalloc((void **)&c->seq, seq_bytes) != hipSuccess)) {
+        (void)hipFree(c->pkts);
         (void)hipFree(c->ctrl);
         delete c;
         return reject(arHipError, "hipMalloc of LL packet memory failed");
     }
     if (hipMemset(c->ctrl, 0, 256) != hipSuccess ||
         (pkt_bytes > 0 && hipMemset(c->pkts, 0, pkt_bytes) != hipSuccess) ||
+        (seq_bytes > 0 && hipMemset(c->seq, 0, seq_bytes) != hipSuccess) ||
         ar::query_ll_residency(c) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(c->seq);
         (void)hipFree(c->pkts);
         (void)hipFree(c->ctrl);
         delete c;
@@ -327,6 +338,8 @@ arResult_t arCommDestroy(arComm_t comm)
     DeviceGuard guard(comm->device);
     arResult_t r = arSuccess;
     if (comm->pkts != nullptr && hipFree(comm->pkts) != hipSuccess)
+        r = arHipError;
+    if (comm->seq != nullptr && hipFree(comm->seq) != hipSuccess)
         r = arHipError;
     if (comm->ctrl != nullptr && hipFree(comm->ctrl) != hipSuccess)
         r = arHipError;
@@ -380,6 +393,8 @@ arResult_t arCommSetOption(arComm_t comm, arOption_t option_arg, int64_t value)
     case arOptHBChunkLayout: ok = value == 0 || value == 1; break;
     case arOptHBGroup: ok = value >= 0 && value <= AR_MAX_RANKS; break;
     case arOptHBStaged: ok = value == 0 || value == 1; break;
+    case arOptLLFlagScheme: ok = value == 0 || value == 1; break;
+    case arOptDebugSeqStart: ok = value >= 0 && value <= 0xffffffffLL; break;
     case arOptLLPacketBytes:
         if (value == 16 && !comm->ll16_ok)
             return reject(arUnsupported, "16-byte packets need packet memory below 4 GiB");
@@ -447,7 +462,10 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
     int threads = (int)comm->opt[ll ? arOptLLThreads : arOptHBThreads];
     uint64_t blocks = (uint64_t)comm->opt[ll ? arOptLLBlocksPerRank : arOptHBBlocks];
     int pkt = ll ? (int)comm->opt[arOptLLPacketBytes] : 0;
-    if (threads == 0 && blocks == 0 && pkt == 0) {
+    // The sequenced LL scheme is an ablation: explicit options or its
+    // defaults, never the tuned shape (the tuner times the cleared scheme).
+    const int scheme = ll ? (int)comm->opt[arOptLLFlagScheme] : ar::kSchemeCleared;
+    if (threads == 0 && blocks == 0 && pkt == 0 && scheme == ar::kSchemeCleared) {
         const ar::TunedShape &t = comm->tuned[dtype][nranks][proto][in_place][bucket_of(bytes)];
         if (t.valid) {
             threads = t.threads;
@@ -465,7 +483,7 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
                                    (int)comm->opt[arOptHBThreads],
                                    (uint64_t)comm->opt[arOptHBBlocks], (hipStream_t)stream)
             : launch(sendbufs, recvbufs, count, dtype, nranks, proto, comm, threads, blocks, pkt,
-                     group, (hipStream_t)stream);
+                     scheme, group, (hipStream_t)stream);
     if (e != hipSuccess)
         return reject(arHipError, hipGetErrorString(e));
     return arSuccess;
@@ -546,9 +564,9 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype_arg, int nranks,
                 const int th = c < 0 ? 0 : (proto == arProtoLL ? kLLThreads[c / nb] : kHBThreads[c / nb]);
                 const int bl = c < 0 ? 0 : (proto == arProtoLL ? kLLBlocks[c % nb] : hb_blocks[c % nb]);
                 float us = 0.0f;
-                const hipError_t e =
-                    time_candidate(send.data(), dst, count, dtype, nranks, (arProtocol_t)proto,
-                                   comm, th, (uint64_t)bl, pkt, calls, cs, e0, e1, &us);
+                const hipError_t e = time_candidate(send.data(), dst, count, dtype, nranks,
+                                                    (arProtocol_t)proto, comm, th, (uint64_t)bl,
+                                                    pkt, ar::kSchemeCleared, calls, cs, e0, e1, &us);
                 if (e != hipSuccess) {
                     result = reject(arHipError, hipGetErrorString(e));
                     break;

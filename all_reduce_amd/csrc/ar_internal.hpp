@@ -17,9 +17,15 @@ enum DType { kBf16 = 0, kFp16 = 1, kFp32 = 2 };
 constexpr int kRankVariants = 6;  // 1, 2, 4, 8, 16, 32 -> exact kernels; others -> generic
 constexpr int kThreadChoices = 5; // 64, 128, 256, 512, 1024
 
+// LL flag schemes (the values of arOptLLFlagScheme): the reader zeroes each
+// consumed packet (the default), or each 512-byte packet group carries a
+// sequence number.
+constexpr int kSchemeCleared = 0;
+constexpr int kSchemeSequenced = 1;
+
 }  // namespace ar
 
-constexpr int kOptionCount = 12;
+constexpr int kOptionCount = 14;
 
 namespace ar {
 // One tuned launch shape: threads per workgroup and workgroups (HB: the
@@ -42,12 +48,15 @@ struct arComm {
     size_t max_ll_bytes;
     int cu_count;
     uint64_t wall_clock_khz;
-    uint64_t *pkts;        // 2 * max_ranks * max_ll_bytes bytes
-    uint64_t pkt_stride;   // packets per rank region
+    uint64_t *pkts;        // 2 * max_ranks * max_ll_bytes bytes, rounded up
+    uint64_t pkt_stride;   // 8-byte packets per rank region, a multiple of 64 (512 bytes)
+    uint32_t *seq;         // sequence table: one entry per 512-byte group and rank region
+    uint64_t seq_words;    // (pkt_stride / 64) * max_ranks
     uint32_t *ctrl;        // control words; [0] is the async error
     int64_t opt[kOptionCount]; // indexed by arOption_t
-    // [packet width: 8 B, 16 B][dtype][rank variant][thread-count index]
-    int ll_resident[2][3][ar::kRankVariants + 1][ar::kThreadChoices];
+    // [flag scheme: cleared, sequenced][packet width: 8 B, 16 B][dtype]
+    // [rank variant][thread-count index]
+    int ll_resident[2][2][3][ar::kRankVariants + 1][ar::kThreadChoices];
     bool ll16_ok;          // the packet scratch is small enough for 16-byte packets
     // [dtype][nranks][protocol][in place][bucket]; filled by arCommTune.  In
     // place and out of place are tuned apart: on MI355X they favour different
@@ -70,15 +79,18 @@ hipError_t launch_hb(const void *const *send, void *const *recv, size_t count, i
                      int nranks, const arComm *comm, int threads, uint64_t blocks, int group,
                      hipStream_t stream);
 // `pkt_bytes` 16 selects 16-byte LL packets (the caller checks comm->ll16_ok),
-// anything else 8-byte packets.
+// anything else 8-byte packets; `scheme` kSchemeSequenced the sequenced flag
+// scheme, anything else the cleared one.
 hipError_t launch_ll(const void *const *send, void *const *recv, size_t count, int dtype,
                      int nranks, const arComm *comm, int threads, uint64_t blocks, int pkt_bytes,
-                     hipStream_t stream);
+                     int scheme, hipStream_t stream);
 // The staged form of the HB two-shot (reduce-scatter into the owner's output,
 // kernel boundary, all-gather from it), flat order only.
 hipError_t launch_hb_staged(const void *const *send, void *const *recv, size_t count, int dtype,
                             int nranks, const arComm *comm, int threads, uint64_t blocks,
                             hipStream_t stream);
+// Zeroes the packets and the error word and sets the sequence table to
+// arOptDebugSeqStart (0 by default).
 hipError_t launch_reset(const arComm *comm, hipStream_t stream);
 // Fills comm->ll_resident from the occupancy calculator.
 hipError_t query_ll_residency(arComm *comm);

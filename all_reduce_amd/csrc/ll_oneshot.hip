@@ -19,26 +19,46 @@
 //           R - 1 of them are written by other workgroups, which for R = 8
 //           sit on the other seven XCDs;
 //   reduce  binary32 sum in rank order 0..R-1, rounded once to the dtype;
-//   clear   the R packets go back to zero;
+//   retire  the R packets are made unable to look ready to a later call;
 //   output  the word goes to all R receive buffers.
 // In place is safe: a word is written out only after all R packets for it
 // arrived, and each packet carries a value its producer had already read.
 //
-// Packet memory is all zero between calls: every packet a call writes is
-// consumed and cleared by the same call, and the next call (on the same
-// stream, or the next node of a replayed graph) starts after this kernel has
-// ended.  So a packet is ready exactly when its flag is nonzero, and no
-// per-call sequence number is needed.  That keeps graph replays correct with
-// frozen kernel arguments and needs no shared counter: a device-wide counter
-// bumped once per workgroup costs a serialised atomic per workgroup on one
-// address, which measured about 15 ns each on MI355X (5 us for the 512
-// workgroups of a 1 MiB-per-rank call).
+// A reader must never take a packet left by an earlier call for a new one.
+// Kernel arguments are frozen in a replayed graph, so the flag value cannot
+// come from the host, and a device-wide call counter would need a serialised
+// atomic per workgroup on one address to advance safely (about 15 ns each on
+// MI355X, 5 us for the 512 workgroups of a 1 MiB-per-rank call).  Two flag
+// schemes avoid both:
+//
+//   cleared    (SEQ = false) the reader zeroes every packet it has consumed,
+//              so packet memory is zero between calls and a packet is ready
+//              when its flag holds the constant kReady.  Costs one store per
+//              packet: a quarter of the scheme's memory traffic.
+//   sequenced  (SEQ = true) every 512-byte group of a rank's packet region has
+//              a 32-bit sequence number in a side table.  Producers write the
+//              group's next number as the flag; the one wave that consumes
+//              the group (the launch aligns every wave's packets to whole
+//              groups) waits for it, then advances the table entry.  Between
+//              calls every nonzero packet of a group carries the entry's
+//              current number, so the next number cannot be mistaken for a
+//              stale one, even after the 32-bit count wraps.  Nothing is
+//              cleared except the packets past the end of the message in its
+//              last group (fewer than 64 per rank).  Every producer reads the
+//              entry before it stores the packets the consumer waits for, so
+//              all reads of an entry precede its update.
+//
+// The schemes interleave freely on one communicator: kReady is a value the
+// sequenced scheme never writes, and a cleared call leaves zeros.  The cleared
+// scheme is the default: on MI355X it is faster at every LL size, because the
+// sequenced scheme's table read sits between a producer's start and its first
+// packet store, while the clears it saves were off the critical path.
 // A wait is bounded by a wall-clock limit: on expiry the lane records
 // arTimeout in the communicator and stops waiting.  Packets of an interrupted
-// call may then stay set, so after arTimeout the communicator must be reset
-// (arCommReset) before further LL calls.  Every workgroup of the grid must be
-// resident at once (the host caps the grid with the occupancy calculator),
-// because consumers wait on producers.
+// call may then stay set and table entries stay behind, so after arTimeout
+// the communicator must be reset (arCommReset) before further LL calls.
+// Every workgroup of the grid must be resident at once (the host caps the
+// grid with the occupancy calculator), because consumers wait on producers.
 #include "ar_internal.hpp"
 #include "ll_packet.hpp"
 
@@ -55,6 +75,8 @@ struct LLParams {
     uint64_t put_per_block;  // packets each workgroup publishes for its rank
     uint64_t get_per_block;  // packets each workgroup polls, reduces and writes out
     uint32_t *ctrl;          // [0] async error (0 or arTimeout)
+    uint32_t *seq;           // sequenced scheme: entry of 512-byte group g, rank j at g * seq_stride + j
+    uint64_t seq_stride;
     uint64_t timeout_ticks;  // wall-clock ticks one packet wait may take
     uint32_t flag_skew;      // test hook: consumers wait for flag + skew
     uint32_t tail_bytes;     // payload bytes of a last, partial packet (0: none)
@@ -70,14 +92,35 @@ constexpr int ll_max_threads(int rmax) { return rmax >= 32 ? 512 : 1024; }
 constexpr int ll_get_batch(int rmax, int pw) { return rmax * pw <= 8 ? 2 : 1; }
 // Source packets' worth of words a lane loads before it stores their packets.
 constexpr int kPutBatch = 8;
-// Flag of a ready packet; cleared packet memory reads 0.
-constexpr uint32_t kReady = 1u;
+// Flag of a ready packet in the cleared scheme; cleared packet memory reads 0,
+// and the sequenced scheme never writes this value.
+constexpr uint32_t kReady = 0xffffffffu;
+// Packets in one 512-byte group of the sequenced scheme.
+constexpr uint64_t seq_group(int pw) { return 64 / pw; }
+
+// The sequence number after s: never 0 (fresh memory) nor kReady.
+__device__ inline uint32_t next_seq(uint32_t s) { return s >= 0xfffffffeu ? 1u : s + 1u; }
+
+// Table entries are read at agent scope, like the packets, and written with
+// ordinary stores: within a call nothing reads an entry after its update (see
+// above), and the kernel boundary makes the writes visible to the next call.
+__device__ inline uint32_t load_seq(const uint32_t *e)
+{
+    return __hip_atomic_load(const_cast<uint32_t *>(e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void store_seq(uint32_t *e, uint32_t v)
+{
+    __hip_atomic_store(e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
 
 // PW: payload words per packet (1: 8-byte packets; 2: 16-byte packets).
-template <typename T, int RMAX, bool EXACT, int PW>
+// SEQ: the sequenced flag scheme, else the cleared one.
+template <typename T, int RMAX, bool EXACT, int PW, bool SEQ>
 __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX> p)
 {
     constexpr int GB = ll_get_batch(RMAX, PW);
+    constexpr uint64_t G = seq_group(PW);
     using IO = PacketIO<PW>;
     using V = typename IO::V;
     const IO io(p.pkts, p.region_bytes);
@@ -99,10 +142,13 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
     const uint64_t pstep = (uint64_t)kPutBatch * nthr;
     for (uint64_t pbase = p0 + threadIdx.x; pbase < pf; pbase += pstep) {
         uint32_t w[kPutBatch][PW];
+        uint32_t sq[kPutBatch];
 #pragma unroll
         for (int v = 0; v < kPutBatch; ++v) {
             const uint64_t q = pbase + (uint64_t)v * nthr;
             if (q < pf) {
+                if constexpr (SEQ)
+                    sq[v] = load_seq(p.seq + (q / G) * p.seq_stride + k);
                 if constexpr (PW == 1) {
                     w[v][0] = src[q];
                 } else {
@@ -121,7 +167,7 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
         for (int v = 0; v < kPutBatch; ++v) {
             const uint64_t q = pbase + (uint64_t)v * nthr;
             if (q < pf)
-                io.store(mine + q, w[v], kReady);
+                io.store(mine + q, w[v], SEQ ? next_seq(sq[v]) : kReady);
         }
     }
     if (p.tail_bytes != 0 && threadIdx.x == 0 && nfull >= p0 && nfull < p1) {
@@ -133,11 +179,25 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
             w[0] = t[0];
         if (p.tail_bytes & 2u)
             w[word ? 1 : 0] = ((const uint16_t *)t)[word ? 2 : 0];
-        io.store(mine + nfull, w, kReady);
+        const uint32_t f =
+            SEQ ? next_seq(load_seq(p.seq + (nfull / G) * p.seq_stride + k)) : kReady;
+        io.store(mine + nfull, w, f);
     }
 
-    // poll, reduce, clear, output: sub-slice k of slice b
-    const uint32_t want = kReady + p.flag_skew;
+    // Sequenced scheme: packets past the message's end in its last group go
+    // back to zero, so that every nonzero packet of a group carries the
+    // group's entry once the entry advances.  No reader touches them.
+    if constexpr (SEQ) {
+        const uint64_t extra = (G - p.npkt % G) % G;
+        if (extra != 0 && blockIdx.x == gridDim.x - 1) {
+            for (uint32_t t = threadIdx.x; t < extra * n; t += nthr)
+                io.clear((uint64_t)(t / extra) * p.pkt_stride + p.npkt + t % extra);
+        }
+    }
+
+    // poll, reduce, retire, output: sub-slice k of slice b
+    // (the debug skew makes the wanted flag one that no producer writes)
+    const uint32_t want_cleared = kReady - p.flag_skew;
     const uint64_t g0 = p0 + (uint64_t)k * p.get_per_block;
     const uint64_t g1 = (g0 + p.get_per_block < p1) ? g0 + p.get_per_block : p1;
     // Two bounds on a lane's total waiting: wall-clock ticks (10 ns each at
@@ -150,15 +210,31 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
     bool gave_up = false;
     for (uint64_t q0 = g0 + threadIdx.x; q0 < g1 && !gave_up; q0 += (uint64_t)GB * nthr) {
         V pk[GB][RMAX];
+        uint32_t sq[SEQ ? GB : 1][SEQ ? RMAX : 1];  // sequenced: the groups' next numbers
 #pragma unroll
         for (int v = 0; v < GB; ++v) {
             const uint64_t q = q0 + (uint64_t)v * nthr;
             if (q < g1) {
+                if constexpr (SEQ) {
+#pragma unroll
+                    for (int j = 0; j < RMAX; ++j)
+                        if (EXACT || j < (int)n)
+                            sq[v][j] = load_seq(p.seq + (q / G) * p.seq_stride + j);
+                }
 #pragma unroll
                 for (int j = 0; j < RMAX; ++j)
                     if (EXACT || j < (int)n)
                         pk[v][j] = io.load((uint64_t)j * p.pkt_stride + q);
             }
+        }
+        if constexpr (SEQ) {
+#pragma unroll
+            for (int v = 0; v < GB; ++v)
+                if (q0 + (uint64_t)v * nthr < g1)
+#pragma unroll
+                    for (int j = 0; j < RMAX; ++j)
+                        if (EXACT || j < (int)n)
+                            sq[v][j] = next_seq(sq[v][j]);
         }
         for (;;) {
             bool ready = true;
@@ -168,7 +244,8 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
 #pragma unroll
                     for (int j = 0; j < RMAX; ++j)
                         if (EXACT || j < (int)n)
-                            ready = ready && IO::ready(pk[v][j], want);
+                            ready = ready && IO::ready(pk[v][j], SEQ ? sq[v][j] + p.flag_skew
+                                                                     : want_cleared);
             if (ready)
                 break;
             const uint64_t now = wall_clock64();
@@ -186,7 +263,8 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
                 if (q < g1) {
 #pragma unroll
                     for (int j = 0; j < RMAX; ++j)
-                        if ((EXACT || j < (int)n) && !IO::ready(pk[v][j], want))
+                        if ((EXACT || j < (int)n) &&
+                            !IO::ready(pk[v][j], SEQ ? sq[v][j] + p.flag_skew : want_cleared))
                             pk[v][j] = io.load((uint64_t)j * p.pkt_stride + q);
                 }
             }
@@ -216,10 +294,22 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
                 }
                 y[e] = T::narrow(acc);
             }
+            if constexpr (SEQ) {
+                // The whole wave has seen its groups' packets (the poll loop
+                // reconverges first); the lane at a group's first packet
+                // advances the group's entries.
+                if (q % G == 0) {
 #pragma unroll
-            for (int j = 0; j < RMAX; ++j)
-                if (EXACT || j < (int)n)
-                    io.clear((uint64_t)j * p.pkt_stride + q);
+                    for (int j = 0; j < RMAX; ++j)
+                        if (EXACT || j < (int)n)
+                            store_seq(p.seq + (q / G) * p.seq_stride + j, sq[v][j]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < RMAX; ++j)
+                    if (EXACT || j < (int)n)
+                        io.clear((uint64_t)j * p.pkt_stride + q);
+            }
             const bool partial = p.tail_bytes != 0 && q == p.npkt - 1;
 #pragma unroll
             for (int r = 0; r < RMAX; ++r) {
@@ -242,14 +332,17 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
     }
 }
 
-// Clears the async-error word and all packets (vector stores; no memset node
-// in graphs).
-__global__ __launch_bounds__(256) void ll_reset(uint64_t *pkts, uint64_t npkts, uint32_t *ctrl)
+// Clears the async-error word and all packets, and sets every sequence-table
+// entry to `seq0` (vector stores; no memset node in graphs).
+__global__ __launch_bounds__(256) void ll_reset(uint64_t *pkts, uint64_t npkts, uint32_t *seq,
+                                                uint64_t nseq, uint32_t seq0, uint32_t *ctrl)
 {
     const uint64_t i0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const uint64_t step = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t i = i0; i < npkts; i += step)
         pkts[i] = 0;
+    for (uint64_t i = i0; i < nseq; i += step)
+        seq[i] = seq0;
     if (i0 < 16)
         ctrl[i0] = 0;
 }
@@ -280,7 +373,7 @@ int variant_of(int nranks)
     }
 }
 
-template <typename T, int RMAX, bool EXACT, int PW>
+template <typename T, int RMAX, bool EXACT, int PW, bool SEQ>
 hipError_t launch_table(const void *const *send, void *const *recv, size_t count, int nranks,
                         const arComm *comm, int want_threads, uint64_t want_blocks,
                         hipStream_t stream)
@@ -298,6 +391,8 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     p.pkt_stride = comm->pkt_stride / PW;
     p.region_bytes = (uint64_t)comm->max_ranks * comm->pkt_stride * sizeof(uint64_t);
     p.ctrl = comm->ctrl;
+    p.seq = comm->seq;
+    p.seq_stride = (uint64_t)comm->max_ranks;
     p.nranks = (uint32_t)nranks;
     p.flag_skew = (uint32_t)comm->opt[arOptDebugFlagSkew];
     p.timeout_ticks = (uint64_t)comm->opt[arOptPollTimeoutUs] * comm->wall_clock_khz / 1000u;
@@ -313,7 +408,7 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     if (threads > ll_max_threads(RMAX))
         threads = ll_max_threads(RMAX);
     const int resident =
-        comm->ll_resident[PW - 1][T::kId][variant_of(nranks)][thread_index(threads)];
+        comm->ll_resident[SEQ ? 1 : 0][PW - 1][T::kId][variant_of(nranks)][thread_index(threads)];
     uint64_t max_per_rank = (uint64_t)(resident / nranks);
     if (max_per_rank < 1)
         max_per_rank = 1;
@@ -333,37 +428,52 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
         per_rank = 1;
     p.put_per_block = (p.npkt + per_rank - 1) / per_rank;
     p.get_per_block = (p.put_per_block + (uint64_t)nranks - 1) / (uint64_t)nranks;
+    if constexpr (SEQ) {
+        // Every sub-slice starts on a group boundary and spans whole groups,
+        // so each group is consumed by one wave (threads is a multiple of 64).
+        // That can only lower the workgroup count.
+        const uint64_t G = seq_group(PW);
+        p.get_per_block = (p.get_per_block + G - 1) / G * G;
+        p.put_per_block = p.get_per_block * (uint64_t)nranks;
+        per_rank = (p.npkt + p.put_per_block - 1) / p.put_per_block;
+    }
     p.blocks_per_rank = (uint32_t)per_rank;
     const uint32_t grid = (uint32_t)(per_rank * (uint64_t)nranks);
 
-    hipLaunchKernelGGL((ll_oneshot<T, RMAX, EXACT, PW>), dim3(grid), dim3(threads), 0, stream, p);
+    hipLaunchKernelGGL((ll_oneshot<T, RMAX, EXACT, PW, SEQ>), dim3(grid), dim3(threads), 0, stream,
+                       p);
     return hipGetLastError();
 }
 
-template <typename T, int PW>
+template <typename T, int PW, bool SEQ>
 hipError_t launch_dtype(const void *const *send, void *const *recv, size_t count, int nranks,
                         const arComm *comm, int th, uint64_t bl, hipStream_t stream)
 {
     switch (nranks) {
-    case 1: return launch_table<T, 1, true, PW>(send, recv, count, nranks, comm, th, bl, stream);
-    case 2: return launch_table<T, 2, true, PW>(send, recv, count, nranks, comm, th, bl, stream);
-    case 4: return launch_table<T, 4, true, PW>(send, recv, count, nranks, comm, th, bl, stream);
-    case 8: return launch_table<T, 8, true, PW>(send, recv, count, nranks, comm, th, bl, stream);
-    case 16: return launch_table<T, 16, true, PW>(send, recv, count, nranks, comm, th, bl, stream);
-    case 32: return launch_table<T, 32, true, PW>(send, recv, count, nranks, comm, th, bl, stream);
-    default: return launch_table<T, 32, false, PW>(send, recv, count, nranks, comm, th, bl, stream);
+    case 1: return launch_table<T, 1, true, PW, SEQ>(send, recv, count, nranks, comm, th, bl, stream);
+    case 2: return launch_table<T, 2, true, PW, SEQ>(send, recv, count, nranks, comm, th, bl, stream);
+    case 4: return launch_table<T, 4, true, PW, SEQ>(send, recv, count, nranks, comm, th, bl, stream);
+    case 8: return launch_table<T, 8, true, PW, SEQ>(send, recv, count, nranks, comm, th, bl, stream);
+    case 16: return launch_table<T, 16, true, PW, SEQ>(send, recv, count, nranks, comm, th, bl, stream);
+    case 32: return launch_table<T, 32, true, PW, SEQ>(send, recv, count, nranks, comm, th, bl, stream);
+    default: return launch_table<T, 32, false, PW, SEQ>(send, recv, count, nranks, comm, th, bl, stream);
     }
 }
 
 template <typename T>
 hipError_t launch_width(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, int th, uint64_t bl, int pkt_bytes, hipStream_t stream)
+                        const arComm *comm, int th, uint64_t bl, int pkt_bytes, int scheme,
+                        hipStream_t stream)
 {
-    return pkt_bytes == 16 ? launch_dtype<T, 2>(send, recv, count, nranks, comm, th, bl, stream)
-                           : launch_dtype<T, 1>(send, recv, count, nranks, comm, th, bl, stream);
+    const bool seq = scheme == kSchemeSequenced;
+    if (pkt_bytes == 16)
+        return seq ? launch_dtype<T, 2, true>(send, recv, count, nranks, comm, th, bl, stream)
+                   : launch_dtype<T, 2, false>(send, recv, count, nranks, comm, th, bl, stream);
+    return seq ? launch_dtype<T, 1, true>(send, recv, count, nranks, comm, th, bl, stream)
+               : launch_dtype<T, 1, false>(send, recv, count, nranks, comm, th, bl, stream);
 }
 
-template <typename T, int RMAX, bool EXACT, int PW>
+template <typename T, int RMAX, bool EXACT, int PW, bool SEQ>
 hipError_t query_one(int *out)
 {
     for (int i = 0; i < kThreadChoices; ++i) {
@@ -373,7 +483,7 @@ hipError_t query_one(int *out)
         }
         int per_cu = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(&ll_oneshot<T, RMAX, EXACT, PW>),
+            &per_cu, reinterpret_cast<const void *>(&ll_oneshot<T, RMAX, EXACT, PW, SEQ>),
             kThreadOptions[i], 0);
         if (e != hipSuccess)
             return e;
@@ -382,63 +492,76 @@ hipError_t query_one(int *out)
     return hipSuccess;
 }
 
-template <typename T, int PW>
+template <typename T, int PW, bool SEQ>
 hipError_t query_dtype(int (*tab)[kThreadChoices])
 {
     hipError_t e;
-    if ((e = query_one<T, 1, true, PW>(tab[0])) != hipSuccess) return e;
-    if ((e = query_one<T, 2, true, PW>(tab[1])) != hipSuccess) return e;
-    if ((e = query_one<T, 4, true, PW>(tab[2])) != hipSuccess) return e;
-    if ((e = query_one<T, 8, true, PW>(tab[3])) != hipSuccess) return e;
-    if ((e = query_one<T, 16, true, PW>(tab[4])) != hipSuccess) return e;
-    if ((e = query_one<T, 32, true, PW>(tab[5])) != hipSuccess) return e;
-    return query_one<T, 32, false, PW>(tab[6]);
+    if ((e = query_one<T, 1, true, PW, SEQ>(tab[0])) != hipSuccess) return e;
+    if ((e = query_one<T, 2, true, PW, SEQ>(tab[1])) != hipSuccess) return e;
+    if ((e = query_one<T, 4, true, PW, SEQ>(tab[2])) != hipSuccess) return e;
+    if ((e = query_one<T, 8, true, PW, SEQ>(tab[3])) != hipSuccess) return e;
+    if ((e = query_one<T, 16, true, PW, SEQ>(tab[4])) != hipSuccess) return e;
+    if ((e = query_one<T, 32, true, PW, SEQ>(tab[5])) != hipSuccess) return e;
+    return query_one<T, 32, false, PW, SEQ>(tab[6]);
+}
+
+template <int PW, bool SEQ>
+hipError_t query_width(int (*tab)[kRankVariants + 1][kThreadChoices])
+{
+    hipError_t e;
+    if ((e = query_dtype<Bf16, PW, SEQ>(tab[kBf16])) != hipSuccess) return e;
+    if ((e = query_dtype<Fp16, PW, SEQ>(tab[kFp16])) != hipSuccess) return e;
+    return query_dtype<Fp32, PW, SEQ>(tab[kFp32]);
 }
 
 }  // namespace
 
 hipError_t launch_ll(const void *const *send, void *const *recv, size_t count, int dtype,
                      int nranks, const arComm *comm, int threads, uint64_t blocks, int pkt_bytes,
-                     hipStream_t stream)
+                     int scheme, hipStream_t stream)
 {
     switch (dtype) {
     case kBf16:
-        return launch_width<Bf16>(send, recv, count, nranks, comm, threads, blocks, pkt_bytes, stream);
+        return launch_width<Bf16>(send, recv, count, nranks, comm, threads, blocks, pkt_bytes,
+                                  scheme, stream);
     case kFp16:
-        return launch_width<Fp16>(send, recv, count, nranks, comm, threads, blocks, pkt_bytes, stream);
+        return launch_width<Fp16>(send, recv, count, nranks, comm, threads, blocks, pkt_bytes,
+                                  scheme, stream);
     default:
-        return launch_width<Fp32>(send, recv, count, nranks, comm, threads, blocks, pkt_bytes, stream);
+        return launch_width<Fp32>(send, recv, count, nranks, comm, threads, blocks, pkt_bytes,
+                                  scheme, stream);
     }
 }
 
 hipError_t launch_reset(const arComm *comm, hipStream_t stream)
 {
     const uint64_t npkts = (uint64_t)comm->max_ranks * comm->pkt_stride;
-    uint64_t blocks = (npkts + 255) / 256;
+    const uint64_t most = npkts > comm->seq_words ? npkts : comm->seq_words;
+    uint64_t blocks = (most + 255) / 256;
     if (blocks > 4096)
         blocks = 4096;
     if (blocks < 1)
         blocks = 1;
     hipLaunchKernelGGL(ll_reset, dim3((uint32_t)blocks), dim3(256), 0, stream, comm->pkts, npkts,
+                       comm->seq, comm->seq_words, (uint32_t)comm->opt[arOptDebugSeqStart],
                        comm->ctrl);
     return hipGetLastError();
 }
 
 hipError_t query_ll_residency(arComm *comm)
 {
-    int per_cu[2][3][kRankVariants + 1][kThreadChoices] = {};
+    int per_cu[2][2][3][kRankVariants + 1][kThreadChoices] = {};
     hipError_t e;
-    if ((e = query_dtype<Bf16, 1>(per_cu[0][kBf16])) != hipSuccess) return e;
-    if ((e = query_dtype<Fp16, 1>(per_cu[0][kFp16])) != hipSuccess) return e;
-    if ((e = query_dtype<Fp32, 1>(per_cu[0][kFp32])) != hipSuccess) return e;
-    if ((e = query_dtype<Bf16, 2>(per_cu[1][kBf16])) != hipSuccess) return e;
-    if ((e = query_dtype<Fp16, 2>(per_cu[1][kFp16])) != hipSuccess) return e;
-    if ((e = query_dtype<Fp32, 2>(per_cu[1][kFp32])) != hipSuccess) return e;
-    for (int w = 0; w < 2; ++w)
-        for (int d = 0; d < 3; ++d)
-            for (int v = 0; v <= kRankVariants; ++v)
-                for (int t = 0; t < kThreadChoices; ++t)
-                    comm->ll_resident[w][d][v][t] = per_cu[w][d][v][t] * comm->cu_count;
+    if ((e = query_width<1, false>(per_cu[0][0])) != hipSuccess) return e;
+    if ((e = query_width<2, false>(per_cu[0][1])) != hipSuccess) return e;
+    if ((e = query_width<1, true>(per_cu[1][0])) != hipSuccess) return e;
+    if ((e = query_width<2, true>(per_cu[1][1])) != hipSuccess) return e;
+    for (int s = 0; s < 2; ++s)
+        for (int w = 0; w < 2; ++w)
+            for (int d = 0; d < 3; ++d)
+                for (int v = 0; v <= kRankVariants; ++v)
+                    for (int t = 0; t < kThreadChoices; ++t)
+                        comm->ll_resident[s][w][d][v][t] = per_cu[s][w][d][v][t] * comm->cu_count;
     return hipSuccess;
 }
 

@@ -72,8 +72,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--only", choices=["all", "sweep", "prefill", "copy", "c5b"], default="all",
-                    help="run one part (for profiler passes)")
+    ap.add_argument("--only", choices=["all", "sweep", "prefill", "copy", "c5b", "ll_variants"],
+                    default="all", help="run one part (for profiler passes and ablations)")
     ap.add_argument("--configs", action="store_true",
                     help="also measure every named workload and print the full table")
     ap.add_argument("--no-tune", action="store_true",
@@ -429,6 +429,37 @@ def main():
             log(f"C5b R={R}: {us:.1f} us per launch, {gbps(R, n, 4, us):.0f} GB/s")
             del sv, rv
         result["c5b_hb"] = rows
+
+    # ---- LL flag scheme x packet width at the default shape, over the sweep ---
+    if args.only == "ll_variants":
+        opt = B.ar.arOption
+        rows = []
+        for k in SWEEP:
+            case = inputs.sweep(k)
+            n = case["count"]
+            x = inputs.make(**case)
+            sv, rv = B.planes(x)
+            row = {"bytes_per_rank": 2 * n}
+            for scheme, sname in ((0, "cleared"), (1, "sequenced")):
+                for width in (8, 16):
+                    B.comm.set_option(opt.arOptLLFlagScheme, scheme)
+                    B.comm.set_option(opt.arOptLLPacketBytes, width)
+                    B.launch(sv, rv, n, "ll")
+                    torch.cuda.synchronize()
+                    key = f"{sname}_{width}"
+                    row[f"{key}_parity"] = B.parity(x, rv)
+                    row[f"{key}_us"] = round(B.graph_us(sv, rv, n, "ll"), 3)
+            B.comm.set_option(opt.arOptLLFlagScheme, 0)
+            B.comm.set_option(opt.arOptLLPacketBytes, 0)
+            rows.append(row)
+            log("ll_variants 2^%d: " % k + "  ".join(
+                f"{key[:-3]} {v:.2f}" for key, v in row.items() if key.endswith("_us")))
+            del sv, rv
+        if B.comm.async_error() != B.ar.arResult.arSuccess:
+            raise RuntimeError("LL wait timed out during the LL variant sweep")
+        result["ll_variants"] = rows
+        for key in [k for k in rows[0] if k.endswith("_us")]:
+            result[f"ll_variants_mean_{key}"] = round(statistics.mean(r[key] for r in rows), 3)
 
     # ---- every named workload as one table ----------------------------------
     if args.configs and args.only == "all":

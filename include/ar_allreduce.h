@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define AR_VERSION 10000 /* 1.0.0 */
+#define AR_VERSION 10100 /* 1.1.0 */
 #define AR_MAX_RANKS 32
 
 typedef struct arComm *arComm_t;
@@ -92,8 +92,9 @@ typedef enum {
     arOptHBBlocks = 2,
     /* HB: 1 = non-temporal loads and stores (default), 0 = ordinary ones. */
     arOptHBNonTemporal = 3,
-    /* Test hook: LL consumers wait for flag + value, which no producer ever
-     * writes when value != 0, so every wait times out.  Default 0. */
+    /* Test hook: LL consumers wait for a flag shifted by this value, which no
+     * producer writes when the value is not 0, so every wait times out.
+     * Default 0. */
     arOptDebugFlagSkew = 4,
     /* HB: 16-byte vectors each lane handles per rank per step (1, 2 or 4;
      * capped at 2 above 4 ranks and at 1 above 8); 0 = default (1). */
@@ -135,14 +136,30 @@ typedef enum {
      * more traffic and one more launch.  Launch shape from arOptHBThreads /
      * arOptHBBlocks or the defaults, never the tuned table.  With
      * arOptHBGroup set, HB calls return arUnsupported.  0 (default): fused. */
-    arOptHBStaged = 11
+    arOptHBStaged = 11,
+    /* LL: how a packet left by an earlier call is kept from looking ready.
+     * 0 (default): the reader zeroes every packet it has consumed, so packet
+     * memory is zero between calls (one extra store per packet).  1: every
+     * 512-byte group of a rank's packets carries a 32-bit sequence number in a
+     * table owned by the communicator; producers flag packets with the
+     * group's next number and the group's reader advances it, so nothing is
+     * cleared.  An ablation: slower on MI355X at every LL size, since each
+     * producer reads the table before it can store.  Both give the same
+     * results and may be mixed from call to call.  With 1, the launch shape
+     * comes from the LL options or the defaults, never the tuned table. */
+    arOptLLFlagScheme = 12,
+    /* Test hook: the value arCommReset writes to every sequence-table entry
+     * (0 .. 0xFFFFFFFF; default 0), to exercise the sequence numbers' wrap.
+     * Takes effect at the next arCommReset. */
+    arOptDebugSeqStart = 13
 } arOption_t;
 
 /* Create a communicator on `device` for groups of up to `maxRanks` (1..32)
  * simulated ranks and LL messages of up to `maxLLBytesPerRank` bytes per rank.
  * It owns device memory for the LL packets (2 * maxRanks * maxLLBytesPerRank
- * bytes: packets are half payload, half flags, at either width; all zero
- * between calls) and a word that records an asynchronous error.  maxLLBytesPerRank
+ * bytes, each rank's share rounded up to 512 bytes: packets are half payload,
+ * half flags, at either width), a sequence table of 1/128 of that size (see
+ * arOptLLFlagScheme) and a word that records an asynchronous error.  maxLLBytesPerRank
  * may be 0 (HB only).  Allocates with hipMalloc, so it must not be called
  * while a stream is being captured.  The caller's current device is left
  * unchanged.
@@ -153,11 +170,11 @@ arResult_t arCommCreate(arComm_t *comm, int device, int maxRanks, size_t maxLLBy
 /* Free the communicator.  Work that uses it must have finished. */
 arResult_t arCommDestroy(arComm_t comm);
 
-/* Enqueue, on `stream`, a kernel that clears the LL packets and the
- * asynchronous error, so that the communicator can be used again after a
- * timeout (an LL call that timed out may leave packets set; LL results are
- * undefined until the reset).  No allocation and no memset node: safe to
- * capture in a graph. */
+/* Enqueue, on `stream`, a kernel that clears the LL packets, the sequence
+ * table (to arOptDebugSeqStart, 0 by default) and the asynchronous error, so
+ * that the communicator can be used again after a timeout (an LL call that
+ * timed out may leave packets set; LL results are undefined until the reset).
+ * No allocation and no memset node: safe to capture in a graph. */
 arResult_t arCommReset(arComm_t comm, arStream_t stream);
 
 /* Read the asynchronous error recorded by earlier kernels: arSuccess or
@@ -186,7 +203,9 @@ arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
  * use the stored shape of their size bucket (the message size rounded up to a
  * power of two) and mode (in place: recvbufs[r] == sendbufs[r] for every
  * rank) unless arOptLLThreads/arOptLLBlocksPerRank (LL) or arOptHBThreads/
- * arOptHBBlocks (HB) are set; arProtoAuto then picks the faster protocol.
+ * arOptHBBlocks (HB), arOptLLPacketBytes or arOptLLFlagScheme are set;
+ * arProtoAuto then picks the faster protocol.  LL candidates cover both
+ * packet widths, in the default flag scheme.
  * Tuning again overwrites the table; sizes never tuned use built-in defaults.
  *
  * Each candidate is timed the way latency-sensitive callers run the library:
