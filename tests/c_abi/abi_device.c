@@ -1,7 +1,7 @@
 /* A plain C99 caller of the all-reduce C ABI on the GPU: device memory from
  * the HIP runtime API, no Python and no torch.  R = 8 ranks of integer-valued
- * bf16 (exact sums), out of place and in place, each protocol; every output
- * element is compared with the exact integer sum. */
+ * bf16 (exact sums), out of place and in place, each protocol and both LL flag
+ * schemes; every output element is compared with the exact integer sum. */
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -59,7 +59,13 @@ int main(void)
 
     const arProtocol_t protos[3] = {arProtoLL, arProtoHB, arProtoAuto};
     int failures = 0;
-    for (int inplace = 0; inplace < 2; ++inplace) {
+    /* both LL flag schemes: consumer clears (0, the default), sequence numbers (1) */
+    for (int run = 0; run < 4; ++run) {
+        const int inplace = run % 2, scheme = run / 2;
+        if (arCommSetOption(comm, arOptLLFlagScheme, scheme) != arSuccess) {
+            printf("FAIL: arCommSetOption(arOptLLFlagScheme, %d)\n", scheme);
+            ++failures;
+        }
         for (int p = 0; p < 3; ++p) {
             for (int r = 0; r < R; ++r)
                 if (check_hip(hipMemcpy(sendp[r], host[r], N * 2, hipMemcpyHostToDevice), "H2D"))
@@ -70,7 +76,7 @@ int main(void)
             arResult_t async = arSuccess;
             if (rc != arSuccess || check_hip(hipDeviceSynchronize(), "sync") ||
                 arCommGetAsyncError(comm, &async) != arSuccess || async != arSuccess) {
-                printf("FAIL: call %d/%d: %s\n", p, inplace, arGetErrorString(rc));
+                printf("FAIL: call %d/%d/%d: %s\n", p, inplace, scheme, arGetErrorString(rc));
                 ++failures;
                 continue;
             }
@@ -78,7 +84,8 @@ int main(void)
                 if (check_hip(hipMemcpy(out, dst[r], N * 2, hipMemcpyDeviceToHost), "D2H"))
                     return 1;
                 if (memcmp(out, want, sizeof want) != 0) {
-                    printf("FAIL: protocol %d in place %d rank %d differs\n", p, inplace, r);
+                    printf("FAIL: protocol %d in place %d scheme %d rank %d differs\n", p, inplace,
+                           scheme, r);
                     ++failures;
                 }
             }
