@@ -310,6 +310,10 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
                     if (EXACT || j < (int)n)
                         io.clear((uint64_t)j * p.pkt_stride + q);
             }
+            // Whole words go out at agent scope, written through to memory:
+            // on MI355X that measured 2-4 % faster than write-back stores from
+            // 32 KiB per rank up (the same as the packets, whose clears must
+            // be written through too), and the outputs are not read here.
             const bool partial = p.tail_bytes != 0 && q == p.npkt - 1;
 #pragma unroll
             for (int r = 0; r < RMAX; ++r) {
@@ -322,9 +326,10 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
                         if (p.tail_bytes & 2u)
                             ((uint16_t *)dst)[word ? 2 : 0] = (uint16_t)y[word ? PW - 1 : 0];
                     } else if constexpr (PW == 1) {
-                        *dst = y[0];
+                        __hip_atomic_store(dst, y[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     } else {
-                        *(uint2 *)dst = make_uint2(y[0], y[1]);
+                        __hip_atomic_store((uint64_t *)dst, ((uint64_t)y[1] << 32) | y[0],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
             }
