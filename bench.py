@@ -25,7 +25,9 @@ Default run (inputs resident in HBM before every timed region):
   its own event pair, with the inputs restored from a pristine copy and 512 MiB
   written to flush the last-level cache before each (untimed).
 * graph_floor_us -- the per-call cost of a graph-replayed one-rank, 16-byte
-  call (one workgroup), to split LL latency into launch floor and protocol.
+  call (one workgroup), to split LL latency into launch floor and protocol;
+  ll_mean_above_floor_us is the sweep's mean LL latency minus it (the floor
+  differs from box to box, the protocol's share much less).
 * cpu_baseline -- the CPU oracle (plain C, OpenMP) timed on this host on the
   same LL sweep inputs, a bounded sample (1.5 s of calls per size).
 
@@ -338,6 +340,8 @@ def main():
         x = inputs.make(1, 8, "bf16", "uniform", seed=0)
         sv, rv = B.planes(x)
         result["graph_floor_us"] = round(B.graph_us(sv, rv, 8, "hb"), 3)
+        result["ll_mean_above_floor_us"] = round(
+            statistics.fmean(r["ll_us"] for r in sweep_rows) - result["graph_floor_us"], 3)
         log(f"graph-replayed launch floor: {result['graph_floor_us']:.2f} us per call")
         del sv, rv
 
