@@ -67,19 +67,27 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> Path:
 
 PROBE_SRC = ROOT / "tests" / "gpu_probe" / "convert_probe.hip"
 PROBE_LIB = ROOT / "tests" / "gpu_probe" / "libconvert_probe.so"
+CEILING_SRC = ROOT / "tests" / "gpu_probe" / "hbm_ceiling.hip"
+CEILING_LIB = ROOT / "tests" / "gpu_probe" / "libhbm_ceiling.so"
+
+
+def _build_shared(src: Path, lib: Path, verbose: bool) -> Path:
+    tmp = lib.with_name(lib.name + f".tmp{os.getpid()}")
+    cmd = [HIPCC, *HIP_FLAGS, "-shared", str(src), "-o", str(tmp)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src.name}:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, lib)
+    if verbose:
+        print(f"built {lib}")
+    return lib
 
 
 def build_probe(verbose: bool = False) -> Path:
-    """Test-only converter probe (same flags, same device header)."""
-    tmp = PROBE_LIB.with_name(PROBE_LIB.name + f".tmp{os.getpid()}")
-    cmd = [HIPCC, *HIP_FLAGS, "-shared", str(PROBE_SRC), "-o", str(tmp)]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed for the probe:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, PROBE_LIB)
-    if verbose:
-        print(f"built {PROBE_LIB}")
-    return PROBE_LIB
+    """The GPU probes (same flags): the test-only converter probe, and the HBM
+    ceiling probe that bench.py --only ceilings times.  Returns the former."""
+    _build_shared(CEILING_SRC, CEILING_LIB, verbose)
+    return _build_shared(PROBE_SRC, PROBE_LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -30,6 +30,11 @@ Default run (inputs resident in HBM before every timed region):
   differs from box to box, the protocol's share much less).
 * cpu_baseline -- the CPU oracle (plain C, OpenMP) timed on this host on the
   same LL sweep inputs, a bounded sample (1.5 s of calls per size).
+* hbm_ceilings -- what the memory system delivers for the HB prefill's access
+  shape without its arithmetic (tests/gpu_probe/hbm_ceiling.hip): 8 streams of
+  128 MiB read only, written only, or copied, with HB's tile mapping and
+  128-bit non-temporal accesses, best of a few launch shapes; HB in place is
+  compared with the bound its equal read and write bytes imply.
 
 ``value`` is the mean LL latency per call over the sweep in microseconds
 (lower is better).  Every timed configuration is first checked bit for bit
@@ -74,7 +79,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--only", choices=["all", "sweep", "prefill", "copy", "c5b", "ll_variants"],
+    ap.add_argument("--only", choices=["all", "sweep", "prefill", "copy", "c5b", "ll_variants",
+                                       "ceilings"],
                     default="all", help="run one part (for profiler passes and ablations)")
     ap.add_argument("--configs", action="store_true",
                     help="also measure every named workload and print the full table")
@@ -339,7 +345,9 @@ def main():
         # HB call (one workgroup, one vector), for the latency breakdown.
         x = inputs.make(1, 8, "bf16", "uniform", seed=0)
         sv, rv = B.planes(x)
-        result["graph_floor_us"] = round(B.graph_us(sv, rv, 8, "hb"), 3)
+        # Minimum of five measurements: a lone one-workgroup graph has read up
+        # to 4.5 us on some runs where every real call of the sweep ran faster.
+        result["graph_floor_us"] = round(min(B.graph_us(sv, rv, 8, "hb") for _ in range(5)), 3)
         result["ll_mean_above_floor_us"] = round(
             statistics.fmean(r["ll_us"] for r in sweep_rows) - result["graph_floor_us"], 3)
         log(f"graph-replayed launch floor: {result['graph_floor_us']:.2f} us per call")
@@ -433,6 +441,24 @@ def main():
             log(f"C5b R={R}: {us:.1f} us per launch, {gbps(R, n, 4, us):.0f} GB/s")
             del sv, rv
         result["c5b_hb"] = rows
+
+    # ---- HBM ceilings of the HB access pattern, beside HB itself -------------
+    if args.only in ("all", "ceilings"):
+        ceil = run_ceilings(B, args)
+        rd, wr = ceil["read"]["best_gbps"], ceil["write"]["best_gbps"]
+        mixed = 2.0 / (1.0 / rd + 1.0 / wr)   # equal bytes read and written, one after the other
+        hb = ceil["hb in place"]["gbps"]
+        result["hbm_ceilings"] = {
+            "read_gbps": rd, "write_gbps": wr,
+            "copy_in_place_gbps": ceil["copy in place"]["best_gbps"],
+            "copy_out_of_place_gbps": ceil["copy out of place"]["best_gbps"],
+            "read_write_bound_gbps": round(mixed, 1),
+            "hb_in_place_gbps": hb, "hb_frac_of_read_write_bound": round(hb / mixed, 4),
+            "note": "HB's access shape without its arithmetic (tests/gpu_probe/hbm_ceiling.hip), "
+                    "best of 6 launch shapes per pattern; the read/write bound combines the "
+                    "read-only and write-only ceilings for equal bytes"}
+        if args.only == "ceilings":
+            result["ceilings"] = ceil
 
     # ---- LL flag scheme x packet width at the default shape, over the sweep ---
     if args.only == "ll_variants":
@@ -716,6 +742,86 @@ def run_configs(B, inputs, sweep_rows, result):
             f"{r['oracle_ms_T']} | {r['oracle_gbps_T']} | {r['parity']} |")
     log(f"(T = {T} host threads)")
     return rows
+
+
+def run_ceilings(B, args):
+    """The HB prefill's memory traffic without its arithmetic: the ceiling
+    probe (tests/gpu_probe/hbm_ceiling.hip) reads, writes or copies 8 streams
+    of 128 MiB with HB's tile mapping and 128-bit non-temporal accesses, over
+    a few launch shapes; HB itself runs on the same planes in place and out of
+    place.  GB/s counts the bytes each pattern must move."""
+    import ctypes
+    from pathlib import Path
+    torch, ar = B.torch, B.ar
+    lib_path = Path(__file__).resolve().parent / "tests" / "gpu_probe" / "libhbm_ceiling.so"
+    if not lib_path.exists():
+        raise RuntimeError(f"{lib_path} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(str(lib_path))
+    vp = ctypes.c_void_p
+    lib.hbm_ceiling_run.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), vp, ctypes.c_uint64,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.hbm_ceiling_run.restype = ctypes.c_int
+    R, n = 8, 8192 * 8192                      # bf16 elements per rank: 128 MiB
+    nvec = n * 2 // 16
+    src = torch.empty((R, n), dtype=torch.bfloat16, device=B.dev).normal_()
+    dst = torch.empty_like(src)
+    shapes = [(256, 256), (512, 256), (1024, 256), (2048, 256), (256, 512), (512, 128)]
+    sink = torch.empty(max(g * t for g, t in shapes) * 4, dtype=torch.int32, device=B.dev)
+    sp = (vp * 8)(*[src[j].data_ptr() for j in range(R)])
+    dp = (vp * 8)(*[dst[j].data_ptr() for j in range(R)])
+    gib = 1 << 30
+    patterns = [("read", 0, sp, gib), ("write", 1, dp, gib), ("copy in place", 2, sp, 2 * gib),
+                ("copy out of place", 2, dp, 2 * gib)]
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = B.events()
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1000.0 / reps
+
+    out = {}
+    for name, mode, d, nbytes in patterns:
+        by_shape = {}
+        for g, t in shapes:
+            def fn(mode=mode, d=d, g=g, t=t):
+                rc = lib.hbm_ceiling_run(sp, d, sink.data_ptr(), nvec, mode, g, t,
+                                         torch.cuda.current_stream().cuda_stream)
+                if rc != 0:
+                    raise RuntimeError("hbm_ceiling_run refused its launch")
+            us = timed(fn, args.steps)
+            by_shape[f"{g}x{t}"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        best = max(by_shape, key=by_shape.get)
+        out[name] = {"best_gbps": by_shape[best], "best_shape": best, "gbps_by_shape": by_shape}
+        log(f"ceiling {name}: best {by_shape[best]:.0f} GB/s at {best}")
+    opt = ar.arOption.arOptHBBlocks
+    cus = torch.cuda.get_device_properties(B.dev).multi_processor_count
+    for name, d, blocks in (("hb in place", sp, 0), ("hb out of place", dp, 0),
+                            ("hb out of place, 2 workgroups per CU", dp, 2 * cus)):
+        srcs = [src[j].data_ptr() for j in range(R)]
+        dsts = [src[j].data_ptr() if d is sp else dst[j].data_ptr() for j in range(R)]
+
+        def fn(srcs=srcs, dsts=dsts):
+            rc = ar.arAllReduce(srcs, dsts, n, ar.arDataType.arBfloat16, ar.arRedOp.arSum, R,
+                                ar.arProtocol.arProtoHB, B.comm.handle,
+                                torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise ar.ArError(rc, "arAllReduce")
+        B.comm.set_option(opt, blocks)
+        try:
+            us = timed(fn, args.steps)
+        finally:
+            B.comm.set_option(opt, 0)
+        out[name] = {"us": round(us, 2), "gbps": round(2 * gib / (us * 1e-6) / 1e9, 1),
+                     "shape": f"{blocks} workgroups x default threads" if blocks else "default"}
+        log(f"{name}: {us:.1f} us, {out[name]['gbps']:.0f} GB/s")
+    del src, dst, sink
+    return out
 
 
 def _sources_digest() -> str:
