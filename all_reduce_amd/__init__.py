@@ -68,7 +68,8 @@ AR_MAX_RANKS = 32
 class arTunedShape(ctypes.Structure):
     """Mirror of arTunedShape_t."""
     _fields_ = [("tuned", ctypes.c_int), ("threads", ctypes.c_int), ("blocks", ctypes.c_int),
-                ("packetBytes", ctypes.c_int), ("us", ctypes.c_float)]
+                ("packetBytes", ctypes.c_int), ("nonTemporal", ctypes.c_int),
+                ("us", ctypes.c_float)]
 
 
 class ArError(RuntimeError):
@@ -281,14 +282,15 @@ class Comm:
 
     def tuned_shape(self, dtype, nranks: int, protocol, bytes_per_rank: int,
                     in_place: bool = False):
-        """(threads, blocks, us, packet_bytes) stored for that size and mode --
-        threads and blocks 0 when the built-in default won; packet_bytes 8 or 16
-        for LL, 0 for HB -- or None if never tuned."""
+        """(threads, blocks, us, packet_bytes, non_temporal) stored for that size
+        and mode -- threads and blocks 0 when the built-in default won;
+        packet_bytes 8 or 16 for LL, 0 for HB; non_temporal 1 or 0 for HB, 0 for
+        LL -- or None if never tuned."""
         r, s = arCommGetTunedShape(self.handle, dtype_code(dtype), nranks,
                                    protocol_code(protocol), bytes_per_rank, 1 if in_place else 0)
         if r != 0:
             raise ArError(r, "arCommGetTunedShape")
-        return None if s.tuned == 0 else (s.threads, s.blocks, s.us, s.packetBytes)
+        return None if s.tuned == 0 else (s.threads, s.blocks, s.us, s.packetBytes, s.nonTemporal)
 
     def reset(self, stream=None):
         r = arCommReset(self.handle, self._stream(stream))

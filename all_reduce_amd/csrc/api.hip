@@ -67,7 +67,7 @@ constexpr int64_t kDefaults[kOptionCount] = {
     2000000,  // arOptPollTimeoutUs
     0,        // arOptLLBlocksPerRank (auto)
     0,        // arOptHBBlocks (auto)
-    1,        // arOptHBNonTemporal
+    -1,       // arOptHBNonTemporal (tuned, else non-temporal)
     0,        // arOptDebugFlagSkew
     0,        // arOptHBUnroll (auto)
     0,        // arOptLLThreads (auto)
@@ -156,13 +156,14 @@ arProtocol_t resolve_protocol(const arComm *comm, arDataType_t dtype, int nranks
 
 hipError_t launch(const void *const *send, void *const *recv, size_t count, arDataType_t dtype,
                   int nranks, arProtocol_t proto, const arComm *comm, int threads,
-                  uint64_t blocks, int pkt_bytes, int scheme, int group, hipStream_t stream)
+                  uint64_t blocks, int pkt_bytes, int scheme, int group, bool nt,
+                  hipStream_t stream)
 {
     return proto == arProtoLL
                ? ar::launch_ll(send, recv, count, (int)dtype, nranks, comm, threads, blocks,
                                pkt_bytes, scheme, stream)
                : ar::launch_hb(send, recv, count, (int)dtype, nranks, comm, threads, blocks, group,
-                               stream);
+                               nt, stream);
 }
 
 // Per-call time of one tuning candidate: `calls` launches captured into a HIP
@@ -173,8 +174,8 @@ hipError_t launch(const void *const *send, void *const *recv, size_t count, arDa
 // hundred KiB per rank).
 hipError_t time_candidate(const void *const *send, void *const *dst, size_t count,
                           arDataType_t dtype, int nranks, arProtocol_t proto, const arComm *comm,
-                          int threads, uint64_t blocks, int pkt_bytes, int scheme, int calls,
-                          hipStream_t cs, hipEvent_t e0, hipEvent_t e1, float *us)
+                          int threads, uint64_t blocks, int pkt_bytes, int scheme, bool nt,
+                          int calls, hipStream_t cs, hipEvent_t e0, hipEvent_t e1, float *us)
 {
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
@@ -184,7 +185,7 @@ hipError_t time_candidate(const void *const *send, void *const *dst, size_t coun
     hipError_t le = hipSuccess;
     for (int i = 0; i < calls && le == hipSuccess; ++i)
         le = launch(send, dst, count, dtype, nranks, proto, comm, threads, blocks, pkt_bytes, scheme,
-                    0, cs);
+                    0, nt, cs);
     e = hipStreamEndCapture(cs, &graph);  // always ends the capture
     if (le != hipSuccess)
         e = le;
@@ -382,7 +383,7 @@ arResult_t arCommSetOption(arComm_t comm, arOption_t option_arg, int64_t value)
     case arOptPollTimeoutUs: ok = value >= 1 && value <= 600000000; break;
     case arOptLLBlocksPerRank: ok = value >= 0 && value <= 65536; break;
     case arOptHBBlocks: ok = value >= 0 && value <= (1 << 20); break;
-    case arOptHBNonTemporal: ok = value == 0 || value == 1; break;
+    case arOptHBNonTemporal: ok = value >= -1 && value <= 1; break;
     case arOptDebugFlagSkew: ok = value >= 0 && value <= 65535; break;
     case arOptHBUnroll: ok = value == 0 || value == 1 || value == 2 || value == 4; break;
     case arOptLLThreads:
@@ -465,14 +466,19 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
     // The sequenced LL scheme is an ablation: explicit options or its
     // defaults, never the tuned shape (the tuner times the cleared scheme).
     const int scheme = ll ? (int)comm->opt[arOptLLFlagScheme] : ar::kSchemeCleared;
-    if (threads == 0 && blocks == 0 && pkt == 0 && scheme == ar::kSchemeCleared) {
-        const ar::TunedShape &t = comm->tuned[dtype][nranks][proto][in_place][bucket_of(bytes)];
-        if (t.valid) {
-            threads = t.threads;
-            blocks = (uint64_t)t.blocks;
-            pkt = t.pkt_bytes;
-        }
+    // HB access policy: the option if set (0 or 1), else the tuned entry's,
+    // else non-temporal.
+    int nt = (int)comm->opt[arOptHBNonTemporal];
+    const ar::TunedShape &t = comm->tuned[dtype][nranks][proto][in_place][bucket_of(bytes)];
+    if (threads == 0 && blocks == 0 && pkt == 0 && scheme == ar::kSchemeCleared && t.valid) {
+        threads = t.threads;
+        blocks = (uint64_t)t.blocks;
+        pkt = t.pkt_bytes;
+        if (nt < 0)
+            nt = t.nt;
     }
+    if (nt < 0)
+        nt = 1;
     if (pkt != 16 || !comm->ll16_ok)
         pkt = 8;
     // The staged HB form is an ablation: explicit options or its defaults,
@@ -481,9 +487,10 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
         proto == arProtoHB && staged
             ? ar::launch_hb_staged(sendbufs, recvbufs, count, (int)dtype, nranks, comm,
                                    (int)comm->opt[arOptHBThreads],
-                                   (uint64_t)comm->opt[arOptHBBlocks], (hipStream_t)stream)
+                                   (uint64_t)comm->opt[arOptHBBlocks],
+                                   comm->opt[arOptHBNonTemporal] != 0, (hipStream_t)stream)
             : launch(sendbufs, recvbufs, count, dtype, nranks, proto, comm, threads, blocks, pkt,
-                     scheme, group, (hipStream_t)stream);
+                     scheme, group, nt != 0, (hipStream_t)stream);
     if (e != hipSuccess)
         return reject(arHipError, hipGetErrorString(e));
     return arSuccess;
@@ -553,26 +560,32 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype_arg, int nranks,
             void *const *dst = in_place ? const_cast<void *const *>(send.data()) : recv.data();
             if (proto == arProtoLL && !ll_possible(comm, nranks, bytes))
                 continue;
-            // LL: each packet width gets the default shape and the grid; HB: one pass.
+            // LL: each packet width gets the default shape and the grid.  HB:
+            // the same for each access policy (non-temporal first), unless
+            // the communicator's option fixes it.
             const int nb = proto == arProtoLL ? 7 : 3;
-            const int per_width = 1 + 3 * nb;
-            const int widths = proto == arProtoLL ? (comm->ll16_ok ? 2 : 1) : 1;
-            ar::TunedShape best = {0, 0, 0, 0, 0.0f};
-            for (int cw = 0; cw < widths * per_width && result == arSuccess; ++cw) {
-                const int c = cw % per_width - 1;
-                const int pkt = proto == arProtoLL ? (cw / per_width == 0 ? 8 : 16) : 0;
+            const int per_variant = 1 + 3 * nb;
+            const int nt_opt = (int)comm->opt[arOptHBNonTemporal];
+            const int variants = proto == arProtoLL ? (comm->ll16_ok ? 2 : 1) : (nt_opt < 0 ? 2 : 1);
+            ar::TunedShape best = {0, 0, 0, 0, 0, 0.0f};
+            for (int cw = 0; cw < variants * per_variant && result == arSuccess; ++cw) {
+                const int c = cw % per_variant - 1;
+                const int var = cw / per_variant;
+                const int pkt = proto == arProtoLL ? (var == 0 ? 8 : 16) : 0;
+                const int nt = proto == arProtoLL ? 0 : (nt_opt >= 0 ? nt_opt : (var == 0 ? 1 : 0));
                 const int th = c < 0 ? 0 : (proto == arProtoLL ? kLLThreads[c / nb] : kHBThreads[c / nb]);
                 const int bl = c < 0 ? 0 : (proto == arProtoLL ? kLLBlocks[c % nb] : hb_blocks[c % nb]);
                 float us = 0.0f;
                 const hipError_t e = time_candidate(send.data(), dst, count, dtype, nranks,
                                                     (arProtocol_t)proto, comm, th, (uint64_t)bl,
-                                                    pkt, ar::kSchemeCleared, calls, cs, e0, e1, &us);
+                                                    pkt, ar::kSchemeCleared, nt != 0, calls, cs,
+                                                    e0, e1, &us);
                 if (e != hipSuccess) {
                     result = reject(arHipError, hipGetErrorString(e));
                     break;
                 }
                 if (!best.valid || us < 0.97f * best.us)
-                    best = {1, th, bl, pkt, us};
+                    best = {1, th, bl, pkt, nt, us};
             }
             if (result == arSuccess)
                 comm->tuned[dtype][nranks][proto][in_place][b] = best;
@@ -615,6 +628,7 @@ arResult_t arCommGetTunedShape(arComm_t comm, arDataType_t dtype_arg, int nranks
     shape->threads = t.threads;
     shape->blocks = t.blocks;
     shape->packetBytes = t.pkt_bytes;
+    shape->nonTemporal = t.nt;
     shape->us = t.us;
     return arSuccess;
 }

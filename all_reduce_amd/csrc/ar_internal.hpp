@@ -36,6 +36,7 @@ struct TunedShape {
     int32_t threads;
     int32_t blocks;
     int32_t pkt_bytes;  // LL packet width that won: 8 or 16 (HB: 0)
+    int32_t nt;         // HB: non-temporal (1) or cached (0) accesses won (LL: 0)
     float us;
 };
 // Message sizes are bucketed by ceil(log2(bytes per rank)).
@@ -74,10 +75,11 @@ namespace ar {
 // the launch error.
 // `group` > 0 selects the hierarchical summation order (groups of `group`
 // consecutive ranks first, then the group partials); the caller guarantees
-// 1 < group < nranks and nranks % group == 0.
+// 1 < group < nranks and nranks % group == 0.  `nt` selects non-temporal
+// loads and stores (else ordinary, cached ones).
 hipError_t launch_hb(const void *const *send, void *const *recv, size_t count, int dtype,
                      int nranks, const arComm *comm, int threads, uint64_t blocks, int group,
-                     hipStream_t stream);
+                     bool nt, hipStream_t stream);
 // `pkt_bytes` 16 selects 16-byte LL packets (the caller checks comm->ll16_ok),
 // anything else 8-byte packets; `scheme` kSchemeSequenced the sequenced flag
 // scheme, anything else the cleared one.
@@ -87,7 +89,7 @@ hipError_t launch_ll(const void *const *send, void *const *recv, size_t count, i
 // The staged form of the HB two-shot (reduce-scatter into the owner's output,
 // kernel boundary, all-gather from it), flat order only.
 hipError_t launch_hb_staged(const void *const *send, void *const *recv, size_t count, int dtype,
-                            int nranks, const arComm *comm, int threads, uint64_t blocks,
+                            int nranks, const arComm *comm, int threads, uint64_t blocks, bool nt,
                             hipStream_t stream);
 // Zeroes the packets and the error word and sets the sequence table to
 // arOptDebugSeqStart (0 by default).

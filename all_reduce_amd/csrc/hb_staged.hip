@@ -134,7 +134,7 @@ hipError_t launch_stages(const StagedParams<RMAX> &p, uint32_t grid, uint32_t th
 
 template <typename T, int RMAX, bool EXACT>
 hipError_t launch_table(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, int want_threads, uint64_t want_blocks,
+                        const arComm *comm, int want_threads, uint64_t want_blocks, bool nt,
                         hipStream_t stream)
 {
     constexpr uint64_t kPerVec = 16 / T::kBytes;
@@ -157,41 +157,43 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
         grid = ntiles;
     if (grid < 1)
         grid = 1;
-    return comm->opt[arOptHBNonTemporal] != 0
-               ? launch_stages<T, RMAX, EXACT, true>(p, (uint32_t)grid, threads, stream)
-               : launch_stages<T, RMAX, EXACT, false>(p, (uint32_t)grid, threads, stream);
+    return nt ? launch_stages<T, RMAX, EXACT, true>(p, (uint32_t)grid, threads, stream)
+              : launch_stages<T, RMAX, EXACT, false>(p, (uint32_t)grid, threads, stream);
 }
 
 template <typename T>
 hipError_t launch_dtype(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, int th, uint64_t bl, hipStream_t stream)
+                        const arComm *comm, int th, uint64_t bl, bool nt, hipStream_t stream)
 {
     switch (nranks) {
-    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, comm, th, bl, stream);
-    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, comm, th, bl, stream);
+    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, comm, th, bl, nt, stream);
+    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, comm, th, bl, nt, stream);
+    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, comm, th, bl, nt, stream);
+    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, comm, th, bl, nt, stream);
+    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, comm, th, bl, nt, stream);
+    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, comm, th, bl, nt, stream);
     default: break;
     }
     if (nranks < 8)
-        return launch_table<T, 8, false>(send, recv, count, nranks, comm, th, bl, stream);
+        return launch_table<T, 8, false>(send, recv, count, nranks, comm, th, bl, nt, stream);
     if (nranks < 16)
-        return launch_table<T, 16, false>(send, recv, count, nranks, comm, th, bl, stream);
-    return launch_table<T, 32, false>(send, recv, count, nranks, comm, th, bl, stream);
+        return launch_table<T, 16, false>(send, recv, count, nranks, comm, th, bl, nt, stream);
+    return launch_table<T, 32, false>(send, recv, count, nranks, comm, th, bl, nt, stream);
 }
 
 }  // namespace
 
 hipError_t launch_hb_staged(const void *const *send, void *const *recv, size_t count, int dtype,
-                            int nranks, const arComm *comm, int threads, uint64_t blocks,
+                            int nranks, const arComm *comm, int threads, uint64_t blocks, bool nt,
                             hipStream_t stream)
 {
     switch (dtype) {
-    case kBf16: return launch_dtype<Bf16>(send, recv, count, nranks, comm, threads, blocks, stream);
-    case kFp16: return launch_dtype<Fp16>(send, recv, count, nranks, comm, threads, blocks, stream);
-    default: return launch_dtype<Fp32>(send, recv, count, nranks, comm, threads, blocks, stream);
+    case kBf16:
+        return launch_dtype<Bf16>(send, recv, count, nranks, comm, threads, blocks, nt, stream);
+    case kFp16:
+        return launch_dtype<Fp16>(send, recv, count, nranks, comm, threads, blocks, nt, stream);
+    default:
+        return launch_dtype<Fp32>(send, recv, count, nranks, comm, threads, blocks, nt, stream);
     }
 }
 

@@ -241,7 +241,7 @@ hipError_t launch_unroll(const HBParams<RMAX> &p, uint32_t grid, uint32_t thread
 template <typename T, int RMAX, bool EXACT>
 hipError_t launch_table(const void *const *send, void *const *recv, size_t count, int nranks,
                         const arComm *comm, int want_threads, uint64_t want_blocks, int group,
-                        hipStream_t stream)
+                        bool nt, hipStream_t stream)
 {
     constexpr uint64_t kPerVec = 16 / T::kBytes;
     HBParams<RMAX> p = {};
@@ -259,7 +259,6 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     int u = comm->opt[arOptHBUnroll] > 0 ? (int)comm->opt[arOptHBUnroll] : 1;
     if (u > max_unroll(RMAX))
         u = max_unroll(RMAX);
-    const bool nt = comm->opt[arOptHBNonTemporal] != 0;
     // Default: 256 threads (128 from 32 ranks up), one workgroup per CU --
     // measured on MI355X, fewer loads in flight per CU stream HBM faster.
     uint32_t threads = want_threads > 0 ? (uint32_t)want_threads : (nranks >= 32 ? 128u : 256u);
@@ -285,39 +284,43 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
 
 template <typename T>
 hipError_t launch_dtype(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, int th, uint64_t bl, int grp, hipStream_t stream)
+                        const arComm *comm, int th, uint64_t bl, int grp, bool nt,
+                        hipStream_t stream)
 {
     switch (nranks) {
-    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, comm, th, bl, grp, stream);
-    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, comm, th, bl, grp, stream);
-    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, comm, th, bl, grp, stream);
-    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, comm, th, bl, grp, stream);
-    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, comm, th, bl, grp, stream);
-    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
+    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
+    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
+    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
+    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
+    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
     default: break;
     }
     if (nranks < 4)
-        return launch_table<T, 4, false>(send, recv, count, nranks, comm, th, bl, grp, stream);
+        return launch_table<T, 4, false>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
     if (nranks < 8)
-        return launch_table<T, 8, false>(send, recv, count, nranks, comm, th, bl, grp, stream);
+        return launch_table<T, 8, false>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
     if (nranks < 16)
-        return launch_table<T, 16, false>(send, recv, count, nranks, comm, th, bl, grp, stream);
-    return launch_table<T, 32, false>(send, recv, count, nranks, comm, th, bl, grp, stream);
+        return launch_table<T, 16, false>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
+    return launch_table<T, 32, false>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
 }
 
 }  // namespace
 
 hipError_t launch_hb(const void *const *send, void *const *recv, size_t count, int dtype,
                      int nranks, const arComm *comm, int threads, uint64_t blocks, int group,
-                     hipStream_t stream)
+                     bool nt, hipStream_t stream)
 {
     switch (dtype) {
     case kBf16:
-        return launch_dtype<Bf16>(send, recv, count, nranks, comm, threads, blocks, group, stream);
+        return launch_dtype<Bf16>(send, recv, count, nranks, comm, threads, blocks, group, nt,
+                                  stream);
     case kFp16:
-        return launch_dtype<Fp16>(send, recv, count, nranks, comm, threads, blocks, group, stream);
+        return launch_dtype<Fp16>(send, recv, count, nranks, comm, threads, blocks, group, nt,
+                                  stream);
     default:
-        return launch_dtype<Fp32>(send, recv, count, nranks, comm, threads, blocks, group, stream);
+        return launch_dtype<Fp32>(send, recv, count, nranks, comm, threads, blocks, group, nt,
+                                  stream);
     }
 }
 

@@ -319,6 +319,8 @@ def main():
                                           else list(shape[:2])) if shape else None)
             shape = B.comm.tuned_shape(torch.bfloat16, R, "ll", 2 * n)
             row["ll_packet_bytes"] = shape[3] if shape else 8
+            shape = B.comm.tuned_shape(torch.bfloat16, R, "hb", 2 * n)
+            row["hb_non_temporal"] = bool(shape[4]) if shape else True
             sweep_rows.append(row)
             log(f"sweep 2^{k}: LL {row['ll_us']:.2f} us  HB {row['hb_us']:.2f} us (graph); "
                 f"eager LL {row['ll_eager_us']:.2f} HB {row['hb_eager_us']:.2f} "
@@ -386,6 +388,7 @@ def main():
         shape = B.comm.tuned_shape(torch.bfloat16, R, "hb", 2 * n, in_place=True)
         pre["shape"] = (("default" if shape[0] == 0 and shape[1] == 0 else list(shape[:2]))
                         if shape else None)
+        pre["non_temporal"] = bool(shape[4]) if shape else True
         result["hb_prefill"] = pre
         traffic = _counter_traffic()
         result["roofline"] = {

@@ -90,7 +90,10 @@ typedef enum {
     /* HB: workgroups in the grid (rounded to a multiple of nranks, capped by
      * the message's tiles); 0 = one per compute unit. */
     arOptHBBlocks = 2,
-    /* HB: 1 = non-temporal loads and stores (default), 0 = ordinary ones. */
+    /* HB: 1 = non-temporal loads and stores, 0 = ordinary (cached) ones.
+     * -1 (default): the policy the tuner chose for the message size and mode,
+     * else 1.  On MI355X ordinary accesses win from a few MiB per rank while
+     * the message fits the last-level cache, non-temporal ones above it. */
     arOptHBNonTemporal = 3,
     /* Test hook: LL consumers wait for a flag shifted by this value, which no
      * producer writes when the value is not 0, so every wait times out.
@@ -205,7 +208,8 @@ arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
  * rank) unless arOptLLThreads/arOptLLBlocksPerRank (LL) or arOptHBThreads/
  * arOptHBBlocks (HB), arOptLLPacketBytes or arOptLLFlagScheme are set;
  * arProtoAuto then picks the faster protocol.  LL candidates cover both
- * packet widths, in the default flag scheme.
+ * packet widths, in the default flag scheme; HB candidates both access
+ * policies unless arOptHBNonTemporal fixes one.
  * Tuning again overwrites the table; sizes never tuned use built-in defaults.
  *
  * Each candidate is timed the way latency-sensitive callers run the library:
@@ -228,6 +232,7 @@ typedef struct {
     int threads;      /* threads per workgroup that won; 0 with blocks 0: the default shape */
     int blocks;       /* workgroups that won (HB: the grid; LL: per rank) */
     int packetBytes;  /* LL: the packet width that won, 8 or 16; HB: 0 */
+    int nonTemporal;  /* HB: 1 if non-temporal accesses won, 0 if cached ones; LL: 0 */
     float us;         /* time per call measured for it, in microseconds */
 } arTunedShape_t;
 

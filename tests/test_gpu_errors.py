@@ -65,6 +65,12 @@ def test_option_ranges(comm):
         comm.set_option(ar.arOption.arOptLLThreads, 96)
     comm.set_option(ar.arOption.arOptHBUnroll, 4)
     assert comm.get_option(ar.arOption.arOptHBUnroll) == 4
+    # HB access policy: -1 (tuned, the default), 0 or 1
+    with ar.Comm(device="cuda:0", max_ranks=2, max_ll_bytes_per_rank=0) as fresh:
+        assert fresh.get_option(ar.arOption.arOptHBNonTemporal) == -1
+    for bad in (-2, 2):
+        with pytest.raises(ar.ArError):
+            comm.set_option(ar.arOption.arOptHBNonTemporal, bad)
 
 
 def test_two_communicators_on_two_streams_at_once(orc):

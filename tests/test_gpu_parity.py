@@ -173,7 +173,7 @@ def test_signed_zeros_and_one_hot(comm, protocol, dtype):
 # ---- launch configurations do not change the bits -----------------------------
 @pytest.mark.parametrize("opt,values", [
     (ar.arOption.arOptHBUnroll, [1, 2, 4]),
-    (ar.arOption.arOptHBNonTemporal, [0, 1]),
+    (ar.arOption.arOptHBNonTemporal, [0, 1, -1]),
     (ar.arOption.arOptHBBlocks, [8, 40, 256, 2048]),
     (ar.arOption.arOptHBThreads, [64, 512, 1024]),
     (ar.arOption.arOptHBChunkLayout, [0, 1]),

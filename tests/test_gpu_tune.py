@@ -32,11 +32,11 @@ def test_table_covers_the_tuned_sizes(comm, in_place):
     for b in range(9, 23):
         hb = comm.tuned_shape(torch.bfloat16, 8, "hb", 1 << b, in_place)
         assert hb is not None and hb[0] in (0, 128, 256, 512) and hb[2] > 0
-        assert hb[3] == 0
+        assert hb[3] == 0 and hb[4] in (0, 1)
         ll = comm.tuned_shape(torch.bfloat16, 8, "ll", 1 << b, in_place)
         if (1 << b) <= comm.max_ll_bytes_per_rank:
             assert ll is not None and ll[0] in (0, 256, 512, 1024) and ll[2] > 0
-            assert ll[3] in (8, 16)
+            assert ll[3] in (8, 16) and ll[4] == 0
         else:
             assert ll is None, "LL cannot run above maxLLBytesPerRank"
     # sizes round up to their bucket; untuned dtype / rank counts stay untuned
