@@ -61,6 +61,21 @@ def test_grouped_matches_grouped_oracle(comm, orc, dtype, R, group, N):
     check(got, expect_grouped(orc, x, group), dtype, f"grouped R={R} g={group} N={N}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("R,group", [(16, 8), (32, 4), (32, 16), (8, 2), (24, 8)])
+def test_grouped_with_cached_accesses(comm, orc, dtype, R, group):
+    """The hierarchical kernels with ordinary (cached) loads and stores, the
+    policy the tuner can pick: compile-time and run-time node sizes."""
+    x = inputs.make(R, 70_001, dtype, "outliers", seed=190 + R + group)
+    try:
+        comm.set_option(ar.arOption.arOptHBNonTemporal, 0)
+        with grouped(comm, group):
+            got = run_allreduce(comm, x, "hb")
+    finally:
+        comm.set_option(ar.arOption.arOptHBNonTemporal, -1)
+    check(got, expect_grouped(orc, x, group), dtype, f"grouped cached R={R} g={group}")
+
+
 def test_grouped_in_place_and_auto(comm, orc):
     x = inputs.make(16, 100_003, "bf16", "outliers", seed=95)
     want = expect_grouped(orc, x, 8)

@@ -98,6 +98,25 @@ def test_tails_and_rank_counts(comm, orc, dtype, R, N, protocol):
     check(comm, orc, x, protocol)
 
 
+@pytest.mark.parametrize("unroll", [1, 2, 4])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 13, 16, 32])
+def test_hb_cached_access_policy(comm, orc, unroll, dtype, R):
+    """Ordinary (cached) loads and stores -- the policy the tuner picks where a
+    message fits the last-level cache -- are separate instantiations of the HB
+    kernel: every rank table, dtype and vectors-per-lane count, with a ragged
+    tail and several tiles."""
+    x = inputs.make(R, 70_001, dtype, "outliers", seed=4000 + 7 * R + unroll)
+    try:
+        comm.set_option(ar.arOption.arOptHBNonTemporal, 0)
+        comm.set_option(ar.arOption.arOptHBUnroll, unroll)
+        check(comm, orc, x, "hb", what=f"hb cached R={R} {dtype} unroll {unroll}")
+        check(comm, orc, x, "hb", inplace=True, what=f"hb cached in place R={R} {dtype}")
+    finally:
+        comm.set_option(ar.arOption.arOptHBNonTemporal, -1)
+        comm.set_option(ar.arOption.arOptHBUnroll, 0)
+
+
 @pytest.mark.parametrize("protocol", ["ll", "hb"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_several_hb_tiles_and_ragged_chunks(comm, orc, protocol, dtype):
