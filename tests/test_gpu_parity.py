@@ -98,20 +98,21 @@ def test_tails_and_rank_counts(comm, orc, dtype, R, N, protocol):
     check(comm, orc, x, protocol)
 
 
+@pytest.mark.parametrize("nt", [0, 1])
 @pytest.mark.parametrize("unroll", [1, 2, 4])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 13, 16, 32])
-def test_hb_cached_access_policy(comm, orc, unroll, dtype, R):
-    """Ordinary (cached) loads and stores -- the policy the tuner picks where a
-    message fits the last-level cache -- are separate instantiations of the HB
-    kernel: every rank table, dtype and vectors-per-lane count, with a ragged
-    tail and several tiles."""
+def test_hb_access_policy_and_unroll(comm, orc, nt, unroll, dtype, R):
+    """Each access policy (non-temporal, or ordinary cached loads and stores,
+    which the tuner picks where a message fits the last-level cache) and each
+    vectors-per-lane count is a separate instantiation of the HB kernel: every
+    rank table and dtype, with a ragged tail and several tiles."""
     x = inputs.make(R, 70_001, dtype, "outliers", seed=4000 + 7 * R + unroll)
     try:
-        comm.set_option(ar.arOption.arOptHBNonTemporal, 0)
+        comm.set_option(ar.arOption.arOptHBNonTemporal, nt)
         comm.set_option(ar.arOption.arOptHBUnroll, unroll)
-        check(comm, orc, x, "hb", what=f"hb cached R={R} {dtype} unroll {unroll}")
-        check(comm, orc, x, "hb", inplace=True, what=f"hb cached in place R={R} {dtype}")
+        check(comm, orc, x, "hb", what=f"hb nt={nt} R={R} {dtype} unroll {unroll}")
+        check(comm, orc, x, "hb", inplace=True, what=f"hb nt={nt} in place R={R} {dtype}")
     finally:
         comm.set_option(ar.arOption.arOptHBNonTemporal, -1)
         comm.set_option(ar.arOption.arOptHBUnroll, 0)
