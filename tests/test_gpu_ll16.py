@@ -49,7 +49,7 @@ def test_c3_decode(comm, orc):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 13, 16, 32])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8, 13, 16, 24, 32])
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 9, 1023, 1025, 1026, 65536 + 5])
 def test_tails_and_rank_counts(comm, orc, dtype, R, N):
     x = inputs.make(R, N, dtype, "normal", seed=3000 + R * 31 + N)

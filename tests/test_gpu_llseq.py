@@ -65,7 +65,7 @@ def test_c3_decode(comm, orc, width):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 13, 16, 32])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8, 13, 16, 24, 32])
 @pytest.mark.parametrize("N", [1, 3, 7, 9, 255, 257, 1023, 1025, 65536 + 5])
 def test_tails_and_rank_counts(comm, orc, width, dtype, R, N):
     x = inputs.make(R, N, dtype, "normal", seed=5000 + R * 31 + N)

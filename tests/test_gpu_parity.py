@@ -90,7 +90,7 @@ def test_c5_fp32_integer_sums_full_size(comm, orc, R):
 
 # ---- shapes, tails and rank counts --------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 13, 16, 32])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8, 13, 16, 24, 32])
 @pytest.mark.parametrize("N", [1, 2, 3, 7, 9, 1023, 1025, 65536 + 5])
 @pytest.mark.parametrize("protocol", ["ll", "hb"])
 def test_tails_and_rank_counts(comm, orc, dtype, R, N, protocol):
@@ -101,7 +101,7 @@ def test_tails_and_rank_counts(comm, orc, dtype, R, N, protocol):
 @pytest.mark.parametrize("nt", [0, 1])
 @pytest.mark.parametrize("unroll", [1, 2, 4])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 13, 16, 32])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8, 13, 16, 24, 32])
 def test_hb_access_policy_and_unroll(comm, orc, nt, unroll, dtype, R):
     """Each access policy (non-temporal, or ordinary cached loads and stores,
     which the tuner picks where a message fits the last-level cache) and each

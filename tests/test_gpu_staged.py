@@ -25,7 +25,7 @@ def comm():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 13, 16, 32])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8, 13, 16, 24, 32])
 @pytest.mark.parametrize("N", [1, 7, 9, 1029, 262144 + 13])
 def test_matches_oracle(comm, orc, dtype, R, N):
     x = inputs.make(R, N, dtype, "outliers" if N > 1000 else "normal", seed=4000 + R * 7 + N)
