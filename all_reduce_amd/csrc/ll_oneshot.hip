@@ -50,9 +50,11 @@
 //
 // The schemes interleave freely on one communicator: kReady is a value the
 // sequenced scheme never writes, and a cleared call leaves zeros.  The cleared
-// scheme is the default: on MI355X it is faster at every LL size, because the
-// sequenced scheme's table read sits between a producer's start and its first
-// packet store, while the clears it saves were off the critical path.
+// scheme is the default: on MI355X it is faster at every LL size.  At small
+// sizes the sequenced scheme's table read sits between a producer's start and
+// its first packet store, while the clears it saves were off the critical
+// path; at large sizes rewriting packet lines that were last read, rather than
+// cleared, measured slower even with the table out of the picture.
 // A wait is bounded by a wall-clock limit: on expiry the lane records
 // arTimeout in the communicator and stops waiting.  Packets of an interrupted
 // call may then stay set and table entries stay behind, so after arTimeout
