@@ -125,3 +125,53 @@ def test_stress_thousands_of_replayed_calls(comm, orc, protocol, pkt, N):
     finally:
         comm.set_option(ar.arOption.arOptLLPacketBytes, old)
     assert comm.async_error() == ar.arResult.arSuccess
+
+
+@pytest.mark.parametrize("scheme", [0, 1])
+def test_reset_captured_in_a_graph(comm, orc, scheme):
+    """arCommReset enqueues a kernel and records no memset, so it may sit inside
+    a captured graph: a reset followed by LL calls of two inputs, replayed with
+    the outputs poisoned in between, in either LL flag scheme."""
+    R, N, dt = 8, 70_001, "bf16"
+    xa = inputs.make(R, N, dt, "uniform", seed=45)
+    xb = inputs.make(R, N, dt, "uniform", seed=46)
+    want_a, want_b = expect(orc, xa), expect(orc, xb)
+    _, sa = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    _, sb = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    pa, da = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    pb, db = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    for r in range(R):
+        sa[r].copy_(xa[r])
+        sb[r].copy_(xb[r])
+    comm.set_option(ar.arOption.arOptLLFlagScheme, scheme)
+    try:
+        note(f"graph with arCommReset, scheme {scheme}: warm-up")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            comm.reset()
+            call(comm, sa, da, N, dt, "ll")
+            call(comm, sb, db, N, dt, "ll")
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            comm.reset()
+            call(comm, sa, da, N, dt, "ll")
+            call(comm, sb, db, N, dt, "ll")
+        torch.cuda.synchronize()
+        for rep in range(4):
+            note(f"graph with arCommReset, scheme {scheme}: replay {rep}")
+            pa.view(torch.uint8).fill_(0xA5)
+            pb.view(torch.uint8).fill_(0x5A)
+            g.replay()
+            torch.cuda.synchronize()
+            assert_parity(torch.stack([t.cpu() for t in da]), want_a, f"replay {rep} A")
+            assert_parity(torch.stack([t.cpu() for t in db]), want_b, f"replay {rep} B")
+            # an eager call between replays, on the state the graph left
+            call(comm, sb, da, N, dt, "ll")
+            torch.cuda.synchronize()
+            assert_parity(torch.stack([t.cpu() for t in da]), want_b, f"eager after {rep}")
+        assert comm.async_error() == ar.arResult.arSuccess
+    finally:
+        comm.set_option(ar.arOption.arOptLLFlagScheme, 0)
