@@ -27,7 +27,7 @@ Default run (inputs resident in HBM before every timed region):
 * graph_floor_us -- the per-call cost of a graph-replayed one-rank, 16-byte
   call (one workgroup), to split LL latency into launch floor and protocol;
   ll_mean_above_floor_us is the sweep's mean LL latency minus it (the floor
-  differs from box to box, the protocol's share much less).
+  differs from machine to machine, the protocol's share much less).
 * cpu_baseline -- the CPU oracle (plain C, OpenMP) timed on this host on the
   same LL sweep inputs, a bounded sample (1.5 s of calls per size).
 * hbm_ceilings -- what the memory system delivers for the HB prefill's access

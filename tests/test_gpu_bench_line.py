@@ -48,7 +48,7 @@ def test_sweep_line():
     assert [r["bytes_per_rank"] for r in rows] == [2 << k for k in range(10, 20)]
     assert all(r["ll_parity"] and r["hb_parity"] for r in rows)
     assert line["value"] == pytest.approx(sum(r["ll_us"] for r in rows) / len(rows), abs=2e-3)
-    # the floor is a one-workgroup call: below the slowest LL call on any box
+    # the floor is a one-workgroup call: below the slowest LL call on any machine
     assert 0 < line["graph_floor_us"] < max(r["ll_us"] for r in rows)
     assert line["ll_mean_above_floor_us"] == pytest.approx(
         line["value"] - line["graph_floor_us"], abs=2e-3)
