@@ -4,12 +4,13 @@
 // Eight rank streams of 16-byte vectors, walked with the same workgroup-to-
 // tile mapping as the HB two-shot's default layout (workgroup w serves chunk
 // w % 8; chunk c is every 8th tile of blockDim.x vectors starting at tile c),
-// with the same non-temporal 128-bit loads and stores.  Modes:
+// with the same non-temporal 128-bit loads and stores (but for mode 3).  Modes:
 //   0 read   load the 8 streams, fold them with xor, and store one vector per
 //            thread to `sink` at the end (grid * blockDim vectors in all);
 //   1 write  store a vector derived from the index to the 8 streams;
 //   2 copy   load the 8 streams and store them to dst[0..7] at the same
-//            offset (dst == src: in place, the HB prefill's access pattern).
+//            offset (dst == src: in place, the HB prefill's access pattern);
+//   3 write  as mode 1, with ordinary (cached) stores instead of non-temporal.
 // Not part of the library: built by __graft_entry__.build() next to the
 // converter probe, checked by tests/test_gpu_probe_hbm.py, and timed by
 // bench.py --only ceilings.
@@ -39,11 +40,17 @@ __global__ __launch_bounds__(1024) void hbm_ceiling(CeilingParams p)
         const uint64_t i = base + threadIdx.x;
         if (i >= p.nvec)
             continue;
-        if (p.mode == 1) {
+        if (p.mode == 1 || p.mode == 3) {
             const u32x4 v = {(uint32_t)i, (uint32_t)(i >> 32), c, 0x9e3779b9u};
+            if (p.mode == 1) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                __builtin_nontemporal_store(v, p.dst[j] + i);
+                for (int j = 0; j < 8; ++j)
+                    __builtin_nontemporal_store(v, p.dst[j] + i);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    p.dst[j][i] = v;
+            }
             continue;
         }
         u32x4 v[8];
@@ -71,7 +78,7 @@ extern "C" int hbm_ceiling_run(void *const *src, void *const *dst, void *sink, u
                                int mode, int grid, int threads, void *stream)
 {
     if (grid < 8 || grid % 8 != 0 || threads < 64 || threads > 1024 || threads % 64 != 0 ||
-        mode < 0 || mode > 2)
+        mode < 0 || mode > 3)
         return -1;
     CeilingParams p;
     for (int j = 0; j < 8; ++j) {

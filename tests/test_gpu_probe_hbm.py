@@ -69,9 +69,10 @@ def test_copy_in_place_leaves_data(probe):
     assert torch.equal(src.cpu(), host)
 
 
-def test_write_pattern(probe):
+@pytest.mark.parametrize("mode", [1, 3])
+def test_write_pattern(probe, mode):
     _, dst = _planes()
-    assert _run(probe, dst, dst, None, 1) == 0
+    assert _run(probe, dst, dst, None, mode) == 0
     i = np.arange(NVEC, dtype=np.uint64)
     chunk = (i // THREADS) % 8
     want = np.stack([i & 0xFFFFFFFF, i >> 32, chunk, np.full(NVEC, 0x9E3779B9, np.uint64)],
@@ -91,7 +92,7 @@ def test_read_folds_every_vector(probe):
 
 
 @pytest.mark.parametrize("grid,threads,mode", [(7, 256, 0), (0, 256, 1), (64, 100, 2),
-                                               (64, 2048, 2), (64, 256, 3)])
+                                               (64, 2048, 2), (64, 256, 4), (64, 256, -1)])
 def test_bad_launch_shapes_are_refused(probe, grid, threads, mode):
     _, src = _planes()
     assert _run(probe, src, src, None, mode, grid, threads) == -1
