@@ -1,6 +1,7 @@
 /* A plain C99 caller of the all-reduce C ABI, host side only: it needs no GPU.
  * Checks that the header compiles as C, that the library links, and the
  * answers the library gives before it touches a device. */
+#include <stddef.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
@@ -17,8 +18,22 @@ static void expect(int cond, const char *what)
     }
 }
 
-int main(void)
+int main(int argc, char **argv)
 {
+    /* With "layout": print the C layout of the ABI's struct, for the binding's
+     * mirror of it to be checked against. */
+    if (argc > 1 && strcmp(argv[1], "layout") == 0) {
+        printf("arTunedShape_t %zu tuned %zu threads %zu blocks %zu packetBytes %zu "
+               "nonTemporal %zu us %zu\n",
+               sizeof(arTunedShape_t), offsetof(arTunedShape_t, tuned),
+               offsetof(arTunedShape_t, threads), offsetof(arTunedShape_t, blocks),
+               offsetof(arTunedShape_t, packetBytes), offsetof(arTunedShape_t, nonTemporal),
+               offsetof(arTunedShape_t, us));
+        printf("arResult_t %zu arDataType_t %zu arRedOp_t %zu arProtocol_t %zu arOption_t %zu\n",
+               sizeof(arResult_t), sizeof(arDataType_t), sizeof(arRedOp_t),
+               sizeof(arProtocol_t), sizeof(arOption_t));
+        return 0;
+    }
     expect(arGetVersion() == AR_VERSION, "arGetVersion");
     expect(strncmp(arGetErrorString(arSuccess), "arSuccess", 9) == 0, "error string");
     expect(strncmp(arGetErrorString(arTimeout), "arTimeout", 9) == 0, "timeout string");

@@ -6,6 +6,7 @@ read from the library's ``AR_DEBUG=1`` log in a child process.
 """
 import json
 import re
+import ctypes
 import subprocess
 import sys
 
@@ -163,3 +164,23 @@ def test_plain_c_caller_host_side():
         cbuild.build()
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert res.returncode == 0 and res.stdout.strip() == "ok", res.stdout + res.stderr
+
+
+def test_binding_mirrors_the_c_layout():
+    """The ctypes mirror of arTunedShape_t has the C struct's size and field
+    offsets, and the enums are int-sized as the binding assumes."""
+    from c_abi import build as cbuild
+    exe = cbuild.HERE / "abi_host.bin"
+    if not exe.exists() or exe.stat().st_mtime < ar.LIBRARY.stat().st_mtime:
+        cbuild.build()
+    res = subprocess.run([str(exe), "layout"], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0, res.stdout + res.stderr
+    shape_line, enum_line = res.stdout.strip().splitlines()
+    words = shape_line.split()
+    c_layout = {words[i]: int(words[i + 1]) for i in range(0, len(words), 2)}
+    m = ar.arTunedShape
+    py_layout = {"arTunedShape_t": ctypes.sizeof(m)}
+    py_layout.update({name: getattr(m, name).offset for name, _ in m._fields_})
+    assert py_layout == c_layout
+    words = enum_line.split()
+    assert all(int(words[i + 1]) == ctypes.sizeof(ctypes.c_int) for i in range(0, len(words), 2))
