@@ -178,3 +178,29 @@ def test_option_values(comm):
     for good in (0, 8, 16):
         comm.set_option(ar.arOption.arOptLLPacketBytes, good)
         assert comm.get_option(ar.arOption.arOptLLPacketBytes) == good
+
+
+def test_large_packet_region():
+    """A communicator whose packet memory reaches 4 GiB (32 ranks x 64 MiB of LL
+    message per rank): 16-byte packets are refused (their buffer offsets are
+    32-bit), and an LL call with 8-byte packets whose last ranks' packets lie
+    past the 4 GiB mark is exact (integer data, so the sum is known)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    R, N = 32, (64 << 20) // 2
+    with ar.Comm(device="cuda:0", max_ranks=R, max_ll_bytes_per_rank=64 << 20) as big:
+        with pytest.raises(ar.ArError) as err:
+            big.set_option(ar.arOption.arOptLLPacketBytes, 16)
+        assert err.value.code == ar.arResult.arUnsupported
+        big.set_option(ar.arOption.arOptLLPacketBytes, 8)
+        g = torch.Generator(device="cuda").manual_seed(3200)
+        plane, sv = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+        plane.copy_(torch.randint(-4, 5, plane.shape, generator=g, device="cuda").to(torch.bfloat16))
+        want = torch.stack(sv).float().sum(0).to(torch.bfloat16)   # exact: |sum| <= 128
+        _, rv = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+        note("LL, 32 ranks x 64 MiB, packets past 4 GiB")
+        big.all_reduce(sv, rv, protocol="ll")
+        torch.cuda.synchronize()
+        assert big.async_error() == ar.arResult.arSuccess
+        for r in range(R):
+            assert torch.equal(rv[r].view(torch.int16), want.view(torch.int16)), f"rank {r}"
