@@ -247,3 +247,26 @@ def test_option_values(comm):
     comm.set_option(ar.arOption.arOptDebugSeqStart, 0xFFFFFFFF)
     assert comm.get_option(ar.arOption.arOptDebugSeqStart) == 0xFFFFFFFF
     comm.set_option(ar.arOption.arOptDebugSeqStart, 0)
+
+
+@pytest.mark.parametrize("scheme", [0, 1])
+@pytest.mark.parametrize("width", [8, 16])
+def test_odd_ll_limit_uses_the_whole_region(orc, scheme, width):
+    """A communicator whose LL limit (1000 bytes per rank) is no whole number of
+    512-byte packet groups: calls up to the limit, including one that ends a
+    few packets before the end of the rounded region, stay exact in either
+    scheme and width, and one element more is refused."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    with ar.Comm(device="cuda:0", max_ranks=8, max_ll_bytes_per_rank=1000) as small:
+        small.set_option(SCHEME, scheme)
+        small.set_option(WIDTH, width)
+        for i, n in enumerate([500, 499, 1, 257, 500, 64, 500]):
+            x = inputs.make(8, n, "bf16", "uniform", seed=5500 + i)
+            got = run_allreduce(small, x, "ll")
+            assert_parity(got, expect(orc, x), f"limit 1000 B, N={n}, scheme {scheme}")
+        _, bufs = ar.rank_buffers(8, 501, torch.bfloat16, "cuda")
+        with pytest.raises(ar.ArError) as err:
+            small.all_reduce(bufs, protocol="ll")
+        assert err.value.code == ar.arResult.arInvalidUsage
+        assert small.async_error() == ar.arResult.arSuccess
