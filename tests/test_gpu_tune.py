@@ -82,3 +82,24 @@ def test_options_override_the_table(comm, orc):
     finally:
         comm.set_option(ar.arOption.arOptLLThreads, 0)
         comm.set_option(ar.arOption.arOptHBThreads, 0)
+
+
+def test_tuning_up_to_a_size_that_is_no_power_of_two(orc):
+    """The last bucket is timed at the limit itself (5000 bytes here, bucket
+    2^13); sizes in it use that entry, larger buckets stay untuned, and the
+    tuned calls keep their bits."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    with ar.Comm(device="cuda:0", max_ranks=4, max_ll_bytes_per_rank=1 << 16) as c:
+        note("arCommTune fp16 R=4 up to 5000 bytes")
+        c.tune(torch.float16, 4, 5000)
+        for proto in ("ll", "hb"):
+            for b in range(9, 14):
+                assert c.tuned_shape(torch.float16, 4, proto, 1 << b) is not None
+            assert c.tuned_shape(torch.float16, 4, proto, 5000) == c.tuned_shape(
+                torch.float16, 4, proto, 8192)
+            assert c.tuned_shape(torch.float16, 4, proto, 8193) is None
+        for n in (2500, 2049, 17):
+            x = inputs.make(4, n, "fp16", "normal", seed=80 + n)
+            for proto in ("ll", "hb", "auto"):
+                assert_parity(run_allreduce(c, x, proto), expect(orc, x), f"{proto} N={n}")
