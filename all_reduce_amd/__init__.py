@@ -55,7 +55,7 @@ class arOption(IntEnum):
     arOptLLThreads = 6
     arOptHBThreads = 7
     arOptHBChunkLayout = 8
-    arOptHBGroup = 9
+    arOptNodeRanks = 9
     arOptLLPacketBytes = 10
     arOptHBStaged = 11
     arOptLLFlagScheme = 12

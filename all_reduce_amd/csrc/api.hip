@@ -73,7 +73,7 @@ constexpr int64_t kDefaults[kOptionCount] = {
     0,        // arOptLLThreads (auto)
     0,        // arOptHBThreads (auto)
     1,        // arOptHBChunkLayout (interleaved tiles)
-    0,        // arOptHBGroup (flat order)
+    0,        // arOptNodeRanks (flat order)
     0,        // arOptLLPacketBytes (tuned, else 8)
     0,        // arOptHBStaged (fused)
     0,        // arOptLLFlagScheme (cleared)
@@ -140,16 +140,17 @@ bool ll_possible(const arComm *comm, int nranks, size_t bytes)
     return nranks <= comm->max_ranks && bytes <= comm->max_ll_bytes;
 }
 
-// The protocol a call runs: arProtoAuto resolves to the tuned faster one.
+// The protocol a call runs: arProtoAuto resolves to the tuned faster one,
+// and to LL only where LL can run the call (`ll_allowed`).
 arProtocol_t resolve_protocol(const arComm *comm, arDataType_t dtype, int nranks, size_t bytes,
-                              int in_place, arProtocol_t protocol)
+                              int in_place, arProtocol_t protocol, bool ll_allowed)
 {
     if (protocol != arProtoAuto)
         return protocol;
     const int b = bucket_of(bytes);
     const ar::TunedShape &ll = comm->tuned[dtype][nranks][arProtoLL][in_place][b];
     const ar::TunedShape &hb = comm->tuned[dtype][nranks][arProtoHB][in_place][b];
-    if (ll_possible(comm, nranks, bytes) && ll.valid && (!hb.valid || ll.us < hb.us))
+    if (ll_allowed && ll_possible(comm, nranks, bytes) && ll.valid && (!hb.valid || ll.us < hb.us))
         return arProtoLL;
     return arProtoHB;
 }
@@ -161,7 +162,7 @@ hipError_t launch(const void *const *send, void *const *recv, size_t count, arDa
 {
     return proto == arProtoLL
                ? ar::launch_ll(send, recv, count, (int)dtype, nranks, comm, threads, blocks,
-                               pkt_bytes, scheme, stream)
+                               pkt_bytes, scheme, group, stream)
                : ar::launch_hb(send, recv, count, (int)dtype, nranks, comm, threads, blocks, group,
                                nt, stream);
 }
@@ -220,7 +221,7 @@ hipError_t time_candidate(const void *const *send, void *const *dst, size_t coun
 // Ranks per simulated node when a hierarchical order is in force, else 0.
 int hierarchy_group(const arComm *comm, int nranks)
 {
-    const int g = (int)comm->opt[arOptHBGroup];
+    const int g = (int)comm->opt[arOptNodeRanks];
     return g > 1 && g < nranks ? g : 0;
 }
 
@@ -392,7 +393,7 @@ arResult_t arCommSetOption(arComm_t comm, arOption_t option_arg, int64_t value)
         break;
     case arOptHBThreads: ok = value >= 0 && value <= 1024 && value % 64 == 0; break;
     case arOptHBChunkLayout: ok = value == 0 || value == 1; break;
-    case arOptHBGroup: ok = value >= 0 && value <= AR_MAX_RANKS; break;
+    case arOptNodeRanks: ok = value >= 0 && value <= AR_MAX_RANKS; break;
     case arOptHBStaged: ok = value == 0 || value == 1; break;
     case arOptLLFlagScheme: ok = value == 0 || value == 1; break;
     case arOptDebugSeqStart: ok = value >= 0 && value <= 0xffffffffLL; break;
@@ -438,14 +439,17 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
     for (int r = 0; r < nranks; ++r)
         in_place &= sendbufs[r] == recvbufs[r] ? 1 : 0;
     if (group != 0 && nranks % group != 0)
-        return reject(arInvalidUsage, "nranks is not a multiple of arOptHBGroup");
-    if (group != 0 && protocol == arProtoLL)
-        return reject(arUnsupported, "LL sums in the flat order only (arOptHBGroup is set)");
+        return reject(arInvalidUsage, "nranks is not a multiple of arOptNodeRanks");
+    // The hierarchical order is built into the fused HB kernel and the LL
+    // kernel of the cleared flag scheme; the two ablations keep the flat order.
     const bool staged = comm->opt[arOptHBStaged] != 0;
-    if (group != 0 && staged)
+    const bool seq_ll = comm->opt[arOptLLFlagScheme] == ar::kSchemeSequenced;
+    const arProtocol_t proto = resolve_protocol(comm, dtype, nranks, bytes, in_place, protocol,
+                                                group == 0 || !seq_ll);
+    if (group != 0 && proto == arProtoLL && seq_ll)
+        return reject(arUnsupported, "the sequenced LL scheme sums in the flat order only");
+    if (group != 0 && proto == arProtoHB && staged)
         return reject(arUnsupported, "the staged HB form sums in the flat order only");
-    const arProtocol_t proto =
-        group != 0 ? arProtoHB : resolve_protocol(comm, dtype, nranks, bytes, in_place, protocol);
     if (proto == arProtoLL) {
         if (nranks > comm->max_ranks)
             return reject(arInvalidUsage, "nranks above the communicator's maxRanks");

@@ -23,6 +23,12 @@ constexpr int kThreadChoices = 5; // 64, 128, 256, 512, 1024
 constexpr int kSchemeCleared = 0;
 constexpr int kSchemeSequenced = 1;
 
+// LL kernel kinds with their own occupancy: the cleared scheme in the flat
+// order, the sequenced scheme (flat order only), the cleared scheme in the
+// hierarchical order.
+constexpr int kLLKinds = 3;
+constexpr int ll_kind(bool seq, bool grouped) { return grouped ? 2 : (seq ? 1 : 0); }
+
 }  // namespace ar
 
 constexpr int kOptionCount = 14;
@@ -55,9 +61,9 @@ struct arComm {
     uint64_t seq_words;    // (pkt_stride / 64) * max_ranks
     uint32_t *ctrl;        // control words; [0] is the async error
     int64_t opt[kOptionCount]; // indexed by arOption_t
-    // [flag scheme: cleared, sequenced][packet width: 8 B, 16 B][dtype]
+    // [kernel kind (ar::ll_kind)][packet width: 8 B, 16 B][dtype]
     // [rank variant][thread-count index]
-    int ll_resident[2][2][3][ar::kRankVariants + 1][ar::kThreadChoices];
+    int ll_resident[ar::kLLKinds][2][3][ar::kRankVariants + 1][ar::kThreadChoices];
     bool ll16_ok;          // the packet scratch is small enough for 16-byte packets
     // [dtype][nranks][protocol][in place][bucket]; filled by arCommTune.  In
     // place and out of place are tuned apart: on MI355X they favour different
@@ -82,10 +88,11 @@ hipError_t launch_hb(const void *const *send, void *const *recv, size_t count, i
                      bool nt, hipStream_t stream);
 // `pkt_bytes` 16 selects 16-byte LL packets (the caller checks comm->ll16_ok),
 // anything else 8-byte packets; `scheme` kSchemeSequenced the sequenced flag
-// scheme, anything else the cleared one.
+// scheme, anything else the cleared one.  `group` as for launch_hb; the caller
+// never combines it with the sequenced scheme.
 hipError_t launch_ll(const void *const *send, void *const *recv, size_t count, int dtype,
                      int nranks, const arComm *comm, int threads, uint64_t blocks, int pkt_bytes,
-                     int scheme, hipStream_t stream);
+                     int scheme, int group, hipStream_t stream);
 // The staged form of the HB two-shot (reduce-scatter into the owner's output,
 // kernel boundary, all-gather from it), flat order only.
 hipError_t launch_hb_staged(const void *const *send, void *const *recv, size_t count, int dtype,

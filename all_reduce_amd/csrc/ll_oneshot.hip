@@ -84,6 +84,7 @@ struct LLParams {
     uint32_t tail_bytes;     // payload bytes of a last, partial packet (0: none)
     uint32_t nranks;
     uint32_t blocks_per_rank;
+    uint32_t group;          // hierarchical order: ranks per node (GROUPED kernels only)
 };
 
 // Largest workgroup compiled for a rank-table size (the polled packets of a
@@ -118,7 +119,10 @@ __device__ inline void store_seq(uint32_t *e, uint32_t v)
 
 // PW: payload words per packet (1: 8-byte packets; 2: 16-byte packets).
 // SEQ: the sequenced flag scheme, else the cleared one.
-template <typename T, int RMAX, bool EXACT, int PW, bool SEQ>
+// GROUPED: the hierarchical order -- the ranks form nodes of p.group
+// consecutive ranks, each node's partial is summed in binary32 in rank order,
+// then the partials in node order, then one rounding -- else the flat order.
+template <typename T, int RMAX, bool EXACT, int PW, bool SEQ, bool GROUPED = false>
 __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX> p)
 {
     constexpr int GB = ll_get_batch(RMAX, PW);
@@ -283,16 +287,31 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
 #pragma unroll
             for (int e = 0; e < PW; ++e) {
                 float acc[T::kPerWord];
+                float total[T::kPerWord] = {};
                 T::widen(IO::word(pk[v][0], e), acc);
 #pragma unroll
                 for (int j = 1; j < RMAX; ++j) {
                     if (EXACT || j < (int)n) {
                         float x[T::kPerWord];
                         T::widen(IO::word(pk[v][j], e), x);
+                        if (GROUPED && (uint32_t)j % p.group == 0) {
+                            // a node is complete: fold its partial in
 #pragma unroll
-                        for (int i = 0; i < T::kPerWord; ++i)
-                            acc[i] = acc[i] + x[i];
+                            for (int i = 0; i < T::kPerWord; ++i) {
+                                total[i] = (uint32_t)j == p.group ? acc[i] : total[i] + acc[i];
+                                acc[i] = x[i];
+                            }
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < T::kPerWord; ++i)
+                                acc[i] = acc[i] + x[i];
+                        }
                     }
+                }
+                if constexpr (GROUPED) {
+#pragma unroll
+                    for (int i = 0; i < T::kPerWord; ++i)
+                        acc[i] = total[i] + acc[i];
                 }
                 y[e] = T::narrow(acc);
             }
@@ -380,9 +399,9 @@ int variant_of(int nranks)
     }
 }
 
-template <typename T, int RMAX, bool EXACT, int PW, bool SEQ>
+template <typename T, int RMAX, bool EXACT, int PW, bool SEQ, bool GROUPED>
 hipError_t launch_table(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, int want_threads, uint64_t want_blocks,
+                        const arComm *comm, int want_threads, uint64_t want_blocks, int group,
                         hipStream_t stream)
 {
     LLParams<RMAX> p = {};
@@ -401,6 +420,7 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     p.seq = comm->seq;
     p.seq_stride = (uint64_t)comm->max_ranks;
     p.nranks = (uint32_t)nranks;
+    p.group = GROUPED ? (uint32_t)group : 0u;
     p.flag_skew = (uint32_t)comm->opt[arOptDebugFlagSkew];
     p.timeout_ticks = (uint64_t)comm->opt[arOptPollTimeoutUs] * comm->wall_clock_khz / 1000u;
 
@@ -415,7 +435,8 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     if (threads > ll_max_threads(RMAX))
         threads = ll_max_threads(RMAX);
     const int resident =
-        comm->ll_resident[SEQ ? 1 : 0][PW - 1][T::kId][variant_of(nranks)][thread_index(threads)];
+        comm->ll_resident[ll_kind(SEQ, GROUPED)][PW - 1][T::kId][variant_of(nranks)]
+                         [thread_index(threads)];
     uint64_t max_per_rank = (uint64_t)(resident / nranks);
     if (max_per_rank < 1)
         max_per_rank = 1;
@@ -447,40 +468,47 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     p.blocks_per_rank = (uint32_t)per_rank;
     const uint32_t grid = (uint32_t)(per_rank * (uint64_t)nranks);
 
-    hipLaunchKernelGGL((ll_oneshot<T, RMAX, EXACT, PW, SEQ>), dim3(grid), dim3(threads), 0, stream,
-                       p);
+    hipLaunchKernelGGL((ll_oneshot<T, RMAX, EXACT, PW, SEQ, GROUPED>), dim3(grid), dim3(threads), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
-template <typename T, int PW, bool SEQ>
+template <typename T, int PW, bool SEQ, bool G>
 hipError_t launch_dtype(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, int th, uint64_t bl, hipStream_t stream)
+                        const arComm *comm, int th, uint64_t bl, int grp, hipStream_t stream)
 {
     switch (nranks) {
-    case 1: return launch_table<T, 1, true, PW, SEQ>(send, recv, count, nranks, comm, th, bl, stream);
-    case 2: return launch_table<T, 2, true, PW, SEQ>(send, recv, count, nranks, comm, th, bl, stream);
-    case 4: return launch_table<T, 4, true, PW, SEQ>(send, recv, count, nranks, comm, th, bl, stream);
-    case 8: return launch_table<T, 8, true, PW, SEQ>(send, recv, count, nranks, comm, th, bl, stream);
-    case 16: return launch_table<T, 16, true, PW, SEQ>(send, recv, count, nranks, comm, th, bl, stream);
-    case 32: return launch_table<T, 32, true, PW, SEQ>(send, recv, count, nranks, comm, th, bl, stream);
-    default: return launch_table<T, 32, false, PW, SEQ>(send, recv, count, nranks, comm, th, bl, stream);
+    case 1: return launch_table<T, 1, true, PW, SEQ, G>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    case 2: return launch_table<T, 2, true, PW, SEQ, G>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    case 4: return launch_table<T, 4, true, PW, SEQ, G>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    case 8: return launch_table<T, 8, true, PW, SEQ, G>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    case 16: return launch_table<T, 16, true, PW, SEQ, G>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    case 32: return launch_table<T, 32, true, PW, SEQ, G>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    default: return launch_table<T, 32, false, PW, SEQ, G>(send, recv, count, nranks, comm, th, bl, grp, stream);
     }
 }
 
 template <typename T>
 hipError_t launch_width(const void *const *send, void *const *recv, size_t count, int nranks,
                         const arComm *comm, int th, uint64_t bl, int pkt_bytes, int scheme,
-                        hipStream_t stream)
+                        int group, hipStream_t stream)
 {
     const bool seq = scheme == kSchemeSequenced;
+    const int g = group;
+    // The hierarchical order is compiled for the cleared scheme only (the
+    // caller rejects it with the sequenced one).
+    if (group != 0)
+        return pkt_bytes == 16
+                   ? launch_dtype<T, 2, false, true>(send, recv, count, nranks, comm, th, bl, g, stream)
+                   : launch_dtype<T, 1, false, true>(send, recv, count, nranks, comm, th, bl, g, stream);
     if (pkt_bytes == 16)
-        return seq ? launch_dtype<T, 2, true>(send, recv, count, nranks, comm, th, bl, stream)
-                   : launch_dtype<T, 2, false>(send, recv, count, nranks, comm, th, bl, stream);
-    return seq ? launch_dtype<T, 1, true>(send, recv, count, nranks, comm, th, bl, stream)
-               : launch_dtype<T, 1, false>(send, recv, count, nranks, comm, th, bl, stream);
+        return seq ? launch_dtype<T, 2, true, false>(send, recv, count, nranks, comm, th, bl, 0, stream)
+                   : launch_dtype<T, 2, false, false>(send, recv, count, nranks, comm, th, bl, 0, stream);
+    return seq ? launch_dtype<T, 1, true, false>(send, recv, count, nranks, comm, th, bl, 0, stream)
+               : launch_dtype<T, 1, false, false>(send, recv, count, nranks, comm, th, bl, 0, stream);
 }
 
-template <typename T, int RMAX, bool EXACT, int PW, bool SEQ>
+template <typename T, int RMAX, bool EXACT, int PW, bool SEQ, bool G>
 hipError_t query_one(int *out)
 {
     for (int i = 0; i < kThreadChoices; ++i) {
@@ -490,7 +518,7 @@ hipError_t query_one(int *out)
         }
         int per_cu = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(&ll_oneshot<T, RMAX, EXACT, PW, SEQ>),
+            &per_cu, reinterpret_cast<const void *>(&ll_oneshot<T, RMAX, EXACT, PW, SEQ, G>),
             kThreadOptions[i], 0);
         if (e != hipSuccess)
             return e;
@@ -499,44 +527,44 @@ hipError_t query_one(int *out)
     return hipSuccess;
 }
 
-template <typename T, int PW, bool SEQ>
+template <typename T, int PW, bool SEQ, bool G>
 hipError_t query_dtype(int (*tab)[kThreadChoices])
 {
     hipError_t e;
-    if ((e = query_one<T, 1, true, PW, SEQ>(tab[0])) != hipSuccess) return e;
-    if ((e = query_one<T, 2, true, PW, SEQ>(tab[1])) != hipSuccess) return e;
-    if ((e = query_one<T, 4, true, PW, SEQ>(tab[2])) != hipSuccess) return e;
-    if ((e = query_one<T, 8, true, PW, SEQ>(tab[3])) != hipSuccess) return e;
-    if ((e = query_one<T, 16, true, PW, SEQ>(tab[4])) != hipSuccess) return e;
-    if ((e = query_one<T, 32, true, PW, SEQ>(tab[5])) != hipSuccess) return e;
-    return query_one<T, 32, false, PW, SEQ>(tab[6]);
+    if ((e = query_one<T, 1, true, PW, SEQ, G>(tab[0])) != hipSuccess) return e;
+    if ((e = query_one<T, 2, true, PW, SEQ, G>(tab[1])) != hipSuccess) return e;
+    if ((e = query_one<T, 4, true, PW, SEQ, G>(tab[2])) != hipSuccess) return e;
+    if ((e = query_one<T, 8, true, PW, SEQ, G>(tab[3])) != hipSuccess) return e;
+    if ((e = query_one<T, 16, true, PW, SEQ, G>(tab[4])) != hipSuccess) return e;
+    if ((e = query_one<T, 32, true, PW, SEQ, G>(tab[5])) != hipSuccess) return e;
+    return query_one<T, 32, false, PW, SEQ, G>(tab[6]);
 }
 
-template <int PW, bool SEQ>
+template <int PW, bool SEQ, bool G>
 hipError_t query_width(int (*tab)[kRankVariants + 1][kThreadChoices])
 {
     hipError_t e;
-    if ((e = query_dtype<Bf16, PW, SEQ>(tab[kBf16])) != hipSuccess) return e;
-    if ((e = query_dtype<Fp16, PW, SEQ>(tab[kFp16])) != hipSuccess) return e;
-    return query_dtype<Fp32, PW, SEQ>(tab[kFp32]);
+    if ((e = query_dtype<Bf16, PW, SEQ, G>(tab[kBf16])) != hipSuccess) return e;
+    if ((e = query_dtype<Fp16, PW, SEQ, G>(tab[kFp16])) != hipSuccess) return e;
+    return query_dtype<Fp32, PW, SEQ, G>(tab[kFp32]);
 }
 
 }  // namespace
 
 hipError_t launch_ll(const void *const *send, void *const *recv, size_t count, int dtype,
                      int nranks, const arComm *comm, int threads, uint64_t blocks, int pkt_bytes,
-                     int scheme, hipStream_t stream)
+                     int scheme, int group, hipStream_t stream)
 {
     switch (dtype) {
     case kBf16:
         return launch_width<Bf16>(send, recv, count, nranks, comm, threads, blocks, pkt_bytes,
-                                  scheme, stream);
+                                  scheme, group, stream);
     case kFp16:
         return launch_width<Fp16>(send, recv, count, nranks, comm, threads, blocks, pkt_bytes,
-                                  scheme, stream);
+                                  scheme, group, stream);
     default:
         return launch_width<Fp32>(send, recv, count, nranks, comm, threads, blocks, pkt_bytes,
-                                  scheme, stream);
+                                  scheme, group, stream);
     }
 }
 
@@ -557,13 +585,15 @@ hipError_t launch_reset(const arComm *comm, hipStream_t stream)
 
 hipError_t query_ll_residency(arComm *comm)
 {
-    int per_cu[2][2][3][kRankVariants + 1][kThreadChoices] = {};
+    int per_cu[kLLKinds][2][3][kRankVariants + 1][kThreadChoices] = {};
     hipError_t e;
-    if ((e = query_width<1, false>(per_cu[0][0])) != hipSuccess) return e;
-    if ((e = query_width<2, false>(per_cu[0][1])) != hipSuccess) return e;
-    if ((e = query_width<1, true>(per_cu[1][0])) != hipSuccess) return e;
-    if ((e = query_width<2, true>(per_cu[1][1])) != hipSuccess) return e;
-    for (int s = 0; s < 2; ++s)
+    if ((e = query_width<1, false, false>(per_cu[ll_kind(false, false)][0])) != hipSuccess) return e;
+    if ((e = query_width<2, false, false>(per_cu[ll_kind(false, false)][1])) != hipSuccess) return e;
+    if ((e = query_width<1, true, false>(per_cu[ll_kind(true, false)][0])) != hipSuccess) return e;
+    if ((e = query_width<2, true, false>(per_cu[ll_kind(true, false)][1])) != hipSuccess) return e;
+    if ((e = query_width<1, false, true>(per_cu[ll_kind(false, true)][0])) != hipSuccess) return e;
+    if ((e = query_width<2, false, true>(per_cu[ll_kind(false, true)][1])) != hipSuccess) return e;
+    for (int s = 0; s < kLLKinds; ++s)
         for (int w = 0; w < 2; ++w)
             for (int d = 0; d < 3; ++d)
                 for (int v = 0; v <= kRankVariants; ++v)

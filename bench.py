@@ -676,37 +676,42 @@ def run_configs(B, inputs, sweep_rows, result):
         del x, sv, rv
         log(f"C5b R={R} done")
 
-    # NEXT-2: the hierarchical order (nodes of 8 ranks) at the C5 shapes
+    # NEXT-2: the hierarchical order (nodes of 8 ranks) at the C5 shapes, with
+    # each protocol that can run the size
     O = B.ar.arOption
     for R, dtype in ((16, "fp16"), (32, "fp16"), (32, "fp32")):
         case = inputs.integer_case(R, dtype)
         x = inputs.make(**case)
         n = case["count"]
         sv, rv = B.planes(x)
-        B.comm.set_option(O.arOptHBGroup, 8)
-        try:
-            B.launch(sv, rv, n, "hb")
-            torch.cuda.synchronize()
-            par = None
-            if not B.args.no_parity:
-                sample = None if n <= (1 << 18) else torch.randint(
-                    0, n, (1 << 20,), generator=torch.Generator().manual_seed(98))
-                xs = x if sample is None else x[:, sample].contiguous()
-                got = B.np.stack([B.bits(t if sample is None else t[sample.to(t.device)])
-                                  for t in rv])
-                want = B.orc.allreduce_grouped(B.oracle_in(xs), dtype, 8, nthreads=T)
-                want = want.view(B.np.uint32) if dtype == "fp32" else want.view(B.np.uint16)
-                par = bool(B.np.array_equal(got, want))
-            if n <= (1 << 18):
-                us = B.graph_us(sv, rv, n, "hb")
-                mode = "graph, nodes of 8"
-            else:
-                us = B.back_to_back_us(sv, rv, n, "hb", B.args.steps)
-                mode = "back-to-back, nodes of 8"
-        finally:
-            B.comm.set_option(O.arOptHBGroup, 0)
-        add(f"C5{'a' if dtype == 'fp16' else 'b'} R={R} hierarchical", R, dtype, n, "hb", mode,
-            us, par)
+        small = n <= (1 << 18)
+        sample = None if small else torch.randint(
+            0, n, (1 << 20,), generator=torch.Generator().manual_seed(98))
+        want = None
+        if not B.args.no_parity:
+            xs = x if sample is None else x[:, sample].contiguous()
+            want = B.orc.allreduce_grouped(B.oracle_in(xs), dtype, 8, nthreads=T)
+            want = want.view(B.np.uint32) if dtype == "fp32" else want.view(B.np.uint16)
+        for proto in (("hb", "ll") if small else ("hb",)):
+            B.comm.set_option(O.arOptNodeRanks, 8)
+            try:
+                B.launch(sv, rv, n, proto)
+                torch.cuda.synchronize()
+                par = None
+                if want is not None:
+                    got = B.np.stack([B.bits(t if sample is None else t[sample.to(t.device)])
+                                      for t in rv])
+                    par = bool(B.np.array_equal(got, want))
+                if small:
+                    us = B.graph_us(sv, rv, n, proto)
+                    mode = "graph, nodes of 8"
+                else:
+                    us = B.back_to_back_us(sv, rv, n, proto, B.args.steps)
+                    mode = "back-to-back, nodes of 8"
+            finally:
+                B.comm.set_option(O.arOptNodeRanks, 0)
+            add(f"C5{'a' if dtype == 'fp16' else 'b'} R={R} hierarchical", R, dtype, n, proto,
+                mode, us, par)
         del x, sv, rv
         log(f"hierarchical R={R} {dtype} done")
 

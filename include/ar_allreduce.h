@@ -113,16 +113,17 @@ typedef enum {
      * (default; streams all R buffers in address order, which HBM serves
      * faster). */
     arOptHBChunkLayout = 8,
-    /* HB: hierarchical summation order for groups of this many consecutive
-     * ranks ("nodes"): each node's partial is summed in binary32 in rank order,
-     * then the partials in node order, then rounded once -- the result of a
-     * two-level all-reduce that reduces inside each node first and across
+    /* Both protocols: hierarchical summation order for nodes of this many
+     * consecutive ranks: each node's partial is summed in binary32 in rank
+     * order, then the partials in node order, then rounded once -- the result
+     * of a two-level all-reduce that reduces inside each node first and across
      * nodes second ("SGLang 中的 MSCCL++ All-Reduce 基准测试与推理集成指南",
      * section 4.4: multi-node algorithms for TP = 16 / 32).  0 (default), 1
      * or >= nranks: the flat order 0..R-1.  A value in between must divide
-     * nranks (else arInvalidUsage); LL then returns arUnsupported and
-     * arProtoAuto runs HB. */
-    arOptHBGroup = 9,
+     * nranks (else arInvalidUsage).  The two ablations keep the flat order:
+     * with arOptHBStaged, HB returns arUnsupported, and with the sequenced LL
+     * flag scheme, LL does (arProtoAuto then runs HB). */
+    arOptNodeRanks = 9,
     /* LL: packet width in bytes.  8: a 4-byte payload next to a 4-byte flag;
      * 16: two such pairs, written and read as one 16-byte access (half the
      * memory instructions per payload byte).  0 (default): the width the
@@ -138,7 +139,7 @@ typedef enum {
      * its owner to the other outputs.  Same result bits; 2 * bytes per rank
      * more traffic and one more launch.  Launch shape from arOptHBThreads /
      * arOptHBBlocks or the defaults, never the tuned table.  With
-     * arOptHBGroup set, HB calls return arUnsupported.  0 (default): fused. */
+     * arOptNodeRanks set, HB calls return arUnsupported.  0 (default): fused. */
     arOptHBStaged = 11,
     /* LL: how a packet left by an earlier call is kept from looking ready.
      * 0 (default): the reader zeroes every packet it has consumed, so packet
@@ -266,9 +267,9 @@ arResult_t arCommGetTunedShape(arComm_t comm, arDataType_t dtype, int nranks,
  * send buffers may overlap one another (they are only read).
  * LL also needs nranks <= the communicator's maxRanks and count * element
  * size <= its maxLLBytesPerRank (arInvalidUsage otherwise); arProtoAuto only
- * picks LL where it can run.  With a hierarchical order set (arOptHBGroup),
- * nranks must be a multiple of the group (arInvalidUsage otherwise), LL and
- * the staged HB form return arUnsupported, and arProtoAuto runs HB.
+ * picks LL where it can run.  With a hierarchical order set (arOptNodeRanks),
+ * nranks must be a multiple of the node size (arInvalidUsage otherwise), and
+ * the staged HB form and the sequenced LL scheme return arUnsupported.
  *
  * The call only enqueues work and returns; the buffers belong to the caller
  * and must stay valid until the work has run (for a captured graph, as long

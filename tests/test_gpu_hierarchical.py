@@ -1,8 +1,8 @@
-"""The hierarchical (two-level) order, arOptHBGroup, on the GPU.
+"""The hierarchical (two-level) order, arOptNodeRanks, on the GPU.
 
 R ranks form nodes of `group` consecutive ranks; the result is each node's
 binary32 partial (rank order), summed over nodes in order, rounded once.  The
-HB kernel must match the grouped oracle bit for bit; against the flat order it
+HB and LL kernels must match the grouped oracle bit for bit; against the flat order it
 may differ only as two binary32 summation orders may (twice the recursive
 summation bound plus one unit in the last place; one unit where the column
 does not cancel).
@@ -31,10 +31,10 @@ def comm():
 def grouped(comm, group):
     class _Ctx:
         def __enter__(self):
-            comm.set_option(ar.arOption.arOptHBGroup, group)
+            comm.set_option(ar.arOption.arOptNodeRanks, group)
 
         def __exit__(self, *exc):
-            comm.set_option(ar.arOption.arOptHBGroup, 0)
+            comm.set_option(ar.arOption.arOptNodeRanks, 0)
     return _Ctx()
 
 
@@ -50,15 +50,33 @@ def check(got, want, dt, what):
         pins.assert_same_bits(g[r], want[r], dt, f"{what} rank {r}")
 
 
+@pytest.mark.parametrize("protocol", ["hb", "ll"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("R,group", [(16, 8), (32, 8), (32, 4), (32, 16), (16, 2), (8, 4), (4, 2),
                                      (24, 8), (12, 4)])
-@pytest.mark.parametrize("N", [1, 7, 1029, 262144 + 13])
-def test_grouped_matches_grouped_oracle(comm, orc, dtype, R, group, N):
+@pytest.mark.parametrize("N", [1, 7, 1029, 131072 + 13])
+def test_grouped_matches_grouped_oracle(comm, orc, protocol, dtype, R, group, N):
     x = inputs.make(R, N, dtype, "outliers" if N > 1000 else "normal", seed=90 + R + group + N)
     with grouped(comm, group):
-        got = run_allreduce(comm, x, "hb")
-    check(got, expect_grouped(orc, x, group), dtype, f"grouped R={R} g={group} N={N}")
+        got = run_allreduce(comm, x, protocol)
+    check(got, expect_grouped(orc, x, group), dtype, f"grouped {protocol} R={R} g={group} N={N}")
+
+
+@pytest.mark.parametrize("width", [8, 16])
+@pytest.mark.parametrize("R,group", [(16, 8), (32, 4), (8, 2), (24, 8)])
+def test_grouped_ll_packet_widths_in_place(comm, orc, width, R, group):
+    """LL in the hierarchical order with each packet width, in place and out of
+    place, at a size with several slices and a ragged last packet."""
+    x = inputs.make(R, 100_003, "bf16", "outliers", seed=290 + R + group + width)
+    want = expect_grouped(orc, x, group)
+    comm.set_option(ar.arOption.arOptLLPacketBytes, width)
+    try:
+        with grouped(comm, group):
+            check(run_allreduce(comm, x, "ll"), want, "bf16", f"grouped ll{width} R={R}")
+            check(run_allreduce(comm, x, "ll", inplace=True), want, "bf16",
+                  f"grouped ll{width} in place R={R}")
+    finally:
+        comm.set_option(ar.arOption.arOptLLPacketBytes, 0)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
@@ -130,14 +148,30 @@ def test_grouping_rules(comm):
         assert ar.arAllReduce(p, p, 64, 0, 0, 12, 1, comm.handle, s) == ar.arResult.arInvalidUsage
     y = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
     q = [t.data_ptr() for t in y]
-    with grouped(comm, 8):  # LL runs the flat order only
-        assert ar.arAllReduce(q, q, 64, 0, 0, 16, 0, comm.handle, s) == ar.arResult.arUnsupported
-        assert ar.arAllReduce(q, q, 64, 0, 0, 16, 2, comm.handle, s) == ar.arResult.arSuccess
+    with grouped(comm, 8):  # both protocols and auto run the hierarchical order
+        for proto in (0, 1, 2):
+            assert ar.arAllReduce(q, q, 64, 0, 0, 16, proto, comm.handle, s) == ar.arResult.arSuccess
+    # the two ablations keep the flat order
+    for opt, value, proto in ((ar.arOption.arOptLLFlagScheme, 1, 0),
+                              (ar.arOption.arOptHBStaged, 1, 1)):
+        comm.set_option(opt, value)
+        try:
+            with grouped(comm, 8):
+                assert ar.arAllReduce(q, q, 64, 0, 0, 16, proto, comm.handle, s) == \
+                    ar.arResult.arUnsupported
+        finally:
+            comm.set_option(opt, 0)
+    comm.set_option(ar.arOption.arOptLLFlagScheme, 1)
+    try:
+        with grouped(comm, 8):  # auto avoids the sequenced LL scheme under a hierarchy
+            assert ar.arAllReduce(q, q, 64, 0, 0, 16, 2, comm.handle, s) == ar.arResult.arSuccess
+    finally:
+        comm.set_option(ar.arOption.arOptLLFlagScheme, 0)
     with grouped(comm, 16):  # a group of all ranks is the flat order; LL allowed
         assert ar.arAllReduce(q, q, 64, 0, 0, 16, 0, comm.handle, s) == ar.arResult.arSuccess
     torch.cuda.synchronize()
     with pytest.raises(ar.ArError):
-        comm.set_option(ar.arOption.arOptHBGroup, 33)
+        comm.set_option(ar.arOption.arOptNodeRanks, 33)
 
 
 def test_grouped_hand_cases(comm):

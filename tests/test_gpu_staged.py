@@ -103,11 +103,11 @@ def test_hierarchical_order_is_refused(comm):
     y = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
     q = [t.data_ptr() for t in y]
     s = torch.cuda.current_stream().cuda_stream
-    comm.set_option(ar.arOption.arOptHBGroup, 8)
+    comm.set_option(ar.arOption.arOptNodeRanks, 8)
     try:
         assert ar.arAllReduce(q, q, 64, 0, 0, 16, 1, comm.handle, s) == ar.arResult.arUnsupported
     finally:
-        comm.set_option(ar.arOption.arOptHBGroup, 0)
+        comm.set_option(ar.arOption.arOptNodeRanks, 0)
     assert ar.arAllReduce(q, q, 64, 0, 0, 16, 1, comm.handle, s) == ar.arResult.arSuccess
     torch.cuda.synchronize()
     with pytest.raises(ar.ArError):
