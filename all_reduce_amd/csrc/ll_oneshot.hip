@@ -84,7 +84,7 @@ struct LLParams {
     uint32_t tail_bytes;     // payload bytes of a last, partial packet (0: none)
     uint32_t nranks;
     uint32_t blocks_per_rank;
-    uint32_t group;          // hierarchical order: ranks per node (GROUPED kernels only)
+    uint32_t node_starts;    // hierarchical order: bit j set where rank j starts a node, j > 0
 };
 
 // Largest workgroup compiled for a rank-table size (the polled packets of a
@@ -119,9 +119,10 @@ __device__ inline void store_seq(uint32_t *e, uint32_t v)
 
 // PW: payload words per packet (1: 8-byte packets; 2: 16-byte packets).
 // SEQ: the sequenced flag scheme, else the cleared one.
-// GROUPED: the hierarchical order -- the ranks form nodes of p.group
-// consecutive ranks, each node's partial is summed in binary32 in rank order,
-// then the partials in node order, then one rounding -- else the flat order.
+// GROUPED: the hierarchical order -- the ranks form nodes of consecutive
+// ranks (p.node_starts marks where each node after the first begins), each
+// node's partial is summed in binary32 in rank order, then the partials in
+// node order, then one rounding -- else the flat order.
 template <typename T, int RMAX, bool EXACT, int PW, bool SEQ, bool GROUPED = false>
 __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX> p)
 {
@@ -287,18 +288,24 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
 #pragma unroll
             for (int e = 0; e < PW; ++e) {
                 float acc[T::kPerWord];
-                float total[T::kPerWord] = {};
+                // The running total of finished nodes starts at -0, which
+                // leaves the first partial added to it exactly as it is
+                // (x + -0 is x for every binary32 x, signed zeros included).
+                float total[T::kPerWord];
+#pragma unroll
+                for (int i = 0; i < T::kPerWord; ++i)
+                    total[i] = -0.0f;
                 T::widen(IO::word(pk[v][0], e), acc);
 #pragma unroll
                 for (int j = 1; j < RMAX; ++j) {
                     if (EXACT || j < (int)n) {
                         float x[T::kPerWord];
                         T::widen(IO::word(pk[v][j], e), x);
-                        if (GROUPED && (uint32_t)j % p.group == 0) {
+                        if (GROUPED && ((p.node_starts >> j) & 1u)) {
                             // a node is complete: fold its partial in
 #pragma unroll
                             for (int i = 0; i < T::kPerWord; ++i) {
-                                total[i] = (uint32_t)j == p.group ? acc[i] : total[i] + acc[i];
+                                total[i] = total[i] + acc[i];
                                 acc[i] = x[i];
                             }
                         } else {
@@ -420,7 +427,10 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     p.seq = comm->seq;
     p.seq_stride = (uint64_t)comm->max_ranks;
     p.nranks = (uint32_t)nranks;
-    p.group = GROUPED ? (uint32_t)group : 0u;
+    p.node_starts = 0u;
+    if constexpr (GROUPED)
+        for (int j = group; j < nranks; j += group)
+            p.node_starts |= 1u << j;
     p.flag_skew = (uint32_t)comm->opt[arOptDebugFlagSkew];
     p.timeout_ticks = (uint64_t)comm->opt[arOptPollTimeoutUs] * comm->wall_clock_khz / 1000u;
 
