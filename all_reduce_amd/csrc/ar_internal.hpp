@@ -23,11 +23,22 @@ constexpr int kThreadChoices = 5; // 64, 128, 256, 512, 1024
 constexpr int kSchemeCleared = 0;
 constexpr int kSchemeSequenced = 1;
 
+// LL node layouts (the kernels' NODE parameter): the flat order, nodes
+// marked by a run-time bitmask (any node size), or nodes of a compile-time
+// size (2, 4, 8 or 16 ranks; a power-of-two rank count admits no other).
+constexpr int kNodeFlat = 0;
+constexpr int kNodeMask = -1;
+
 // LL kernel kinds with their own occupancy: the cleared scheme in the flat
-// order, the sequenced scheme (flat order only), the cleared scheme in the
-// hierarchical order.
-constexpr int kLLKinds = 3;
-constexpr int ll_kind(bool seq, bool grouped) { return grouped ? 2 : (seq ? 1 : 0); }
+// order, the sequenced scheme (flat order only), then the cleared scheme in
+// the hierarchical order with a node bitmask, or with nodes of 2, 4, 8 or 16.
+constexpr int kLLKinds = 7;
+constexpr int ll_kind(bool seq, int node)
+{
+    return node == kNodeFlat ? (seq ? 1 : 0)
+         : node == kNodeMask ? 2
+         : node == 2 ? 3 : node == 4 ? 4 : node == 8 ? 5 : 6;
+}
 
 }  // namespace ar
 

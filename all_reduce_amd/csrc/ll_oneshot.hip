@@ -84,7 +84,7 @@ struct LLParams {
     uint32_t tail_bytes;     // payload bytes of a last, partial packet (0: none)
     uint32_t nranks;
     uint32_t blocks_per_rank;
-    uint32_t node_starts;    // hierarchical order: bit j set where rank j starts a node, j > 0
+    uint32_t node_starts;    // bitmask node layout: bit j set where rank j starts a node, j > 0
 };
 
 // Largest workgroup compiled for a rank-table size (the polled packets of a
@@ -119,11 +119,15 @@ __device__ inline void store_seq(uint32_t *e, uint32_t v)
 
 // PW: payload words per packet (1: 8-byte packets; 2: 16-byte packets).
 // SEQ: the sequenced flag scheme, else the cleared one.
-// GROUPED: the hierarchical order -- the ranks form nodes of consecutive
-// ranks (p.node_starts marks where each node after the first begins), each
-// node's partial is summed in binary32 in rank order, then the partials in
-// node order, then one rounding -- else the flat order.
-template <typename T, int RMAX, bool EXACT, int PW, bool SEQ, bool GROUPED = false>
+// NODE: kNodeFlat for the flat order, else the hierarchical order -- the
+// ranks form nodes of consecutive ranks, each node's partial is summed in
+// binary32 in rank order, then the partials in node order, then one rounding.
+// Nodes of NODE ranks when NODE > 0, which makes every node boundary a
+// compile-time fact of the unrolled rank loop; with kNodeMask, p.node_starts
+// marks where each node after the first begins, a per-rank select that costs
+// a second addition and two selects per value (on MI355X, 16-byte packets at
+// 32 ranks ran 10-18 % slower with the mask than in the flat order).
+template <typename T, int RMAX, bool EXACT, int PW, bool SEQ, int NODE = kNodeFlat>
 __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX> p)
 {
     constexpr int GB = ll_get_batch(RMAX, PW);
@@ -301,7 +305,12 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
                     if (EXACT || j < (int)n) {
                         float x[T::kPerWord];
                         T::widen(IO::word(pk[v][j], e), x);
-                        if (GROUPED && ((p.node_starts >> j) & 1u)) {
+                        bool starts_node = false;
+                        if constexpr (NODE > 0)
+                            starts_node = j % NODE == 0;
+                        else if constexpr (NODE == kNodeMask)
+                            starts_node = (p.node_starts >> j) & 1u;
+                        if (starts_node) {
                             // a node is complete: fold its partial in
 #pragma unroll
                             for (int i = 0; i < T::kPerWord; ++i) {
@@ -315,7 +324,7 @@ __global__ __launch_bounds__(ll_max_threads(RMAX)) void ll_oneshot(LLParams<RMAX
                         }
                     }
                 }
-                if constexpr (GROUPED) {
+                if constexpr (NODE != kNodeFlat) {
 #pragma unroll
                     for (int i = 0; i < T::kPerWord; ++i)
                         acc[i] = total[i] + acc[i];
@@ -406,7 +415,7 @@ int variant_of(int nranks)
     }
 }
 
-template <typename T, int RMAX, bool EXACT, int PW, bool SEQ, bool GROUPED>
+template <typename T, int RMAX, bool EXACT, int PW, bool SEQ, int NODE>
 hipError_t launch_table(const void *const *send, void *const *recv, size_t count, int nranks,
                         const arComm *comm, int want_threads, uint64_t want_blocks, int group,
                         hipStream_t stream)
@@ -428,7 +437,7 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     p.seq_stride = (uint64_t)comm->max_ranks;
     p.nranks = (uint32_t)nranks;
     p.node_starts = 0u;
-    if constexpr (GROUPED)
+    if constexpr (NODE == kNodeMask)
         for (int j = group; j < nranks; j += group)
             p.node_starts |= 1u << j;
     p.flag_skew = (uint32_t)comm->opt[arOptDebugFlagSkew];
@@ -445,7 +454,7 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     if (threads > ll_max_threads(RMAX))
         threads = ll_max_threads(RMAX);
     const int resident =
-        comm->ll_resident[ll_kind(SEQ, GROUPED)][PW - 1][T::kId][variant_of(nranks)]
+        comm->ll_resident[ll_kind(SEQ, NODE)][PW - 1][T::kId][EXACT ? variant_of(RMAX) : kRankVariants]
                          [thread_index(threads)];
     uint64_t max_per_rank = (uint64_t)(resident / nranks);
     if (max_per_rank < 1)
@@ -478,12 +487,12 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     p.blocks_per_rank = (uint32_t)per_rank;
     const uint32_t grid = (uint32_t)(per_rank * (uint64_t)nranks);
 
-    hipLaunchKernelGGL((ll_oneshot<T, RMAX, EXACT, PW, SEQ, GROUPED>), dim3(grid), dim3(threads), 0,
+    hipLaunchKernelGGL((ll_oneshot<T, RMAX, EXACT, PW, SEQ, NODE>), dim3(grid), dim3(threads), 0,
                        stream, p);
     return hipGetLastError();
 }
 
-template <typename T, int PW, bool SEQ, bool G>
+template <typename T, int PW, bool SEQ, int G>
 hipError_t launch_dtype(const void *const *send, void *const *recv, size_t count, int nranks,
                         const arComm *comm, int th, uint64_t bl, int grp, hipStream_t stream)
 {
@@ -498,27 +507,61 @@ hipError_t launch_dtype(const void *const *send, void *const *recv, size_t count
     }
 }
 
+// The hierarchical order.  A power-of-two rank count has power-of-two node
+// sizes only (a node size divides the rank count), each compiled in; any
+// other rank count takes the bitmask kernel.
+template <typename T, int PW, int RMAX, int NODE>
+hipError_t launch_nodes(const void *const *send, void *const *recv, size_t count, int nranks,
+                        const arComm *comm, int th, uint64_t bl, int grp, hipStream_t stream)
+{
+    if constexpr (NODE < RMAX) {
+        if (grp == NODE)
+            return launch_table<T, RMAX, true, PW, false, NODE>(send, recv, count, nranks, comm,
+                                                                 th, bl, grp, stream);
+        return launch_nodes<T, PW, RMAX, NODE * 2>(send, recv, count, nranks, comm, th, bl, grp,
+                                                   stream);
+    } else {
+        return launch_table<T, 32, false, PW, false, kNodeMask>(send, recv, count, nranks, comm,
+                                                                th, bl, grp, stream);
+    }
+}
+
+template <typename T, int PW>
+hipError_t launch_grouped(const void *const *send, void *const *recv, size_t count, int nranks,
+                          const arComm *comm, int th, uint64_t bl, int grp, hipStream_t stream)
+{
+    switch (nranks) {
+    case 4: return launch_nodes<T, PW, 4, 2>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    case 8: return launch_nodes<T, PW, 8, 2>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    case 16: return launch_nodes<T, PW, 16, 2>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    case 32: return launch_nodes<T, PW, 32, 2>(send, recv, count, nranks, comm, th, bl, grp, stream);
+    default:
+        return launch_table<T, 32, false, PW, false, kNodeMask>(send, recv, count, nranks, comm,
+                                                                th, bl, grp, stream);
+    }
+}
+
 template <typename T>
 hipError_t launch_width(const void *const *send, void *const *recv, size_t count, int nranks,
                         const arComm *comm, int th, uint64_t bl, int pkt_bytes, int scheme,
                         int group, hipStream_t stream)
 {
     const bool seq = scheme == kSchemeSequenced;
-    const int g = group;
+    constexpr int F = kNodeFlat;
     // The hierarchical order is compiled for the cleared scheme only (the
     // caller rejects it with the sequenced one).
     if (group != 0)
         return pkt_bytes == 16
-                   ? launch_dtype<T, 2, false, true>(send, recv, count, nranks, comm, th, bl, g, stream)
-                   : launch_dtype<T, 1, false, true>(send, recv, count, nranks, comm, th, bl, g, stream);
+                   ? launch_grouped<T, 2>(send, recv, count, nranks, comm, th, bl, group, stream)
+                   : launch_grouped<T, 1>(send, recv, count, nranks, comm, th, bl, group, stream);
     if (pkt_bytes == 16)
-        return seq ? launch_dtype<T, 2, true, false>(send, recv, count, nranks, comm, th, bl, 0, stream)
-                   : launch_dtype<T, 2, false, false>(send, recv, count, nranks, comm, th, bl, 0, stream);
-    return seq ? launch_dtype<T, 1, true, false>(send, recv, count, nranks, comm, th, bl, 0, stream)
-               : launch_dtype<T, 1, false, false>(send, recv, count, nranks, comm, th, bl, 0, stream);
+        return seq ? launch_dtype<T, 2, true, F>(send, recv, count, nranks, comm, th, bl, 0, stream)
+                   : launch_dtype<T, 2, false, F>(send, recv, count, nranks, comm, th, bl, 0, stream);
+    return seq ? launch_dtype<T, 1, true, F>(send, recv, count, nranks, comm, th, bl, 0, stream)
+               : launch_dtype<T, 1, false, F>(send, recv, count, nranks, comm, th, bl, 0, stream);
 }
 
-template <typename T, int RMAX, bool EXACT, int PW, bool SEQ, bool G>
+template <typename T, int RMAX, bool EXACT, int PW, bool SEQ, int G>
 hipError_t query_one(int *out)
 {
     for (int i = 0; i < kThreadChoices; ++i) {
@@ -537,7 +580,7 @@ hipError_t query_one(int *out)
     return hipSuccess;
 }
 
-template <typename T, int PW, bool SEQ, bool G>
+template <typename T, int PW, bool SEQ, int G>
 hipError_t query_dtype(int (*tab)[kThreadChoices])
 {
     hipError_t e;
@@ -550,13 +593,44 @@ hipError_t query_dtype(int (*tab)[kThreadChoices])
     return query_one<T, 32, false, PW, SEQ, G>(tab[6]);
 }
 
-template <int PW, bool SEQ, bool G>
+template <int PW, bool SEQ, int G>
 hipError_t query_width(int (*tab)[kRankVariants + 1][kThreadChoices])
 {
     hipError_t e;
     if ((e = query_dtype<Bf16, PW, SEQ, G>(tab[kBf16])) != hipSuccess) return e;
     if ((e = query_dtype<Fp16, PW, SEQ, G>(tab[kFp16])) != hipSuccess) return e;
     return query_dtype<Fp32, PW, SEQ, G>(tab[kFp32]);
+}
+
+// The hierarchical-order kernels that launch_grouped can pick: nodes of NODE
+// ranks at each power-of-two rank count above NODE, or the bitmask kernel.
+template <typename T, int PW, int NODE>
+hipError_t query_nodes(int (*tab)[kThreadChoices])
+{
+    if constexpr (NODE == kNodeMask) {
+        return query_one<T, 32, false, PW, false, kNodeMask>(tab[kRankVariants]);
+    } else {
+        hipError_t e;
+        if constexpr (NODE < 4)
+            if ((e = query_one<T, 4, true, PW, false, NODE>(tab[2])) != hipSuccess) return e;
+        if constexpr (NODE < 8)
+            if ((e = query_one<T, 8, true, PW, false, NODE>(tab[3])) != hipSuccess) return e;
+        if constexpr (NODE < 16)
+            if ((e = query_one<T, 16, true, PW, false, NODE>(tab[4])) != hipSuccess) return e;
+        return query_one<T, 32, true, PW, false, NODE>(tab[5]);
+    }
+}
+
+template <int NODE>
+hipError_t query_grouped(int (*tab)[3][kRankVariants + 1][kThreadChoices])
+{
+    hipError_t e;
+    if ((e = query_nodes<Bf16, 1, NODE>(tab[0][kBf16])) != hipSuccess) return e;
+    if ((e = query_nodes<Fp16, 1, NODE>(tab[0][kFp16])) != hipSuccess) return e;
+    if ((e = query_nodes<Fp32, 1, NODE>(tab[0][kFp32])) != hipSuccess) return e;
+    if ((e = query_nodes<Bf16, 2, NODE>(tab[1][kBf16])) != hipSuccess) return e;
+    if ((e = query_nodes<Fp16, 2, NODE>(tab[1][kFp16])) != hipSuccess) return e;
+    return query_nodes<Fp32, 2, NODE>(tab[1][kFp32]);
 }
 
 }  // namespace
@@ -597,12 +671,16 @@ hipError_t query_ll_residency(arComm *comm)
 {
     int per_cu[kLLKinds][2][3][kRankVariants + 1][kThreadChoices] = {};
     hipError_t e;
-    if ((e = query_width<1, false, false>(per_cu[ll_kind(false, false)][0])) != hipSuccess) return e;
-    if ((e = query_width<2, false, false>(per_cu[ll_kind(false, false)][1])) != hipSuccess) return e;
-    if ((e = query_width<1, true, false>(per_cu[ll_kind(true, false)][0])) != hipSuccess) return e;
-    if ((e = query_width<2, true, false>(per_cu[ll_kind(true, false)][1])) != hipSuccess) return e;
-    if ((e = query_width<1, false, true>(per_cu[ll_kind(false, true)][0])) != hipSuccess) return e;
-    if ((e = query_width<2, false, true>(per_cu[ll_kind(false, true)][1])) != hipSuccess) return e;
+    constexpr int F = kNodeFlat;
+    if ((e = query_width<1, false, F>(per_cu[ll_kind(false, F)][0])) != hipSuccess) return e;
+    if ((e = query_width<2, false, F>(per_cu[ll_kind(false, F)][1])) != hipSuccess) return e;
+    if ((e = query_width<1, true, F>(per_cu[ll_kind(true, F)][0])) != hipSuccess) return e;
+    if ((e = query_width<2, true, F>(per_cu[ll_kind(true, F)][1])) != hipSuccess) return e;
+    if ((e = query_grouped<kNodeMask>(per_cu[ll_kind(false, kNodeMask)])) != hipSuccess) return e;
+    if ((e = query_grouped<2>(per_cu[ll_kind(false, 2)])) != hipSuccess) return e;
+    if ((e = query_grouped<4>(per_cu[ll_kind(false, 4)])) != hipSuccess) return e;
+    if ((e = query_grouped<8>(per_cu[ll_kind(false, 8)])) != hipSuccess) return e;
+    if ((e = query_grouped<16>(per_cu[ll_kind(false, 16)])) != hipSuccess) return e;
     for (int s = 0; s < kLLKinds; ++s)
         for (int w = 0; w < 2; ++w)
             for (int d = 0; d < 3; ++d)

@@ -52,8 +52,8 @@ def check(got, want, dt, what):
 
 @pytest.mark.parametrize("protocol", ["hb", "ll"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("R,group", [(16, 8), (32, 8), (32, 4), (32, 16), (16, 2), (8, 4), (4, 2),
-                                     (24, 8), (12, 4)])
+@pytest.mark.parametrize("R,group", [(16, 8), (32, 8), (32, 4), (32, 16), (32, 2), (16, 4),
+                                     (16, 2), (8, 4), (8, 2), (4, 2), (24, 8), (12, 4), (12, 3)])
 @pytest.mark.parametrize("N", [1, 7, 1029, 131072 + 13])
 def test_grouped_matches_grouped_oracle(comm, orc, protocol, dtype, R, group, N):
     x = inputs.make(R, N, dtype, "outliers" if N > 1000 else "normal", seed=90 + R + group + N)
