@@ -74,7 +74,7 @@ constexpr int64_t kDefaults[kOptionCount] = {
     0,        // arOptHBThreads (auto)
     1,        // arOptHBChunkLayout (interleaved tiles)
     0,        // arOptNodeRanks (flat order)
-    0,        // arOptLLPacketBytes (tuned, else 8)
+    0,        // arOptLLPacketBytes (tuned, else by size)
     0,        // arOptHBStaged (fused)
     0,        // arOptLLFlagScheme (cleared)
     0,        // arOptDebugSeqStart
@@ -216,6 +216,13 @@ hipError_t time_candidate(const void *const *send, void *const *dst, size_t coun
         (void)hipGraphDestroy(graph);
     *us = best;
     return e;
+}
+
+// Default LL packet width: the measured default shape's, when the
+// communicator allows 16-byte packets.
+int default_ll_packet(const arComm *comm, int nranks, size_t bytes_per_rank)
+{
+    return comm->ll16_ok && ar::ll_default_shape(nranks, bytes_per_rank).pkt_bytes == 16 ? 16 : 8;
 }
 
 // Ranks per simulated node when a hierarchical order is in force, else 0.
@@ -483,6 +490,8 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
     }
     if (nt < 0)
         nt = 1;
+    if (pkt == 0)
+        pkt = default_ll_packet(comm, nranks, bytes);
     if (pkt != 16 || !comm->ll16_ok)
         pkt = 8;
     // The staged HB form is an ablation: explicit options or its defaults,
@@ -544,7 +553,7 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype_arg, int nranks,
     // to what the kernel and the message allow.  A candidate replaces the best
     // so far only if it is more than 3 % faster, so timing noise does not move
     // the choice away from the default.
-    static const int kLLThreads[] = {256, 512, 1024};
+    static const int kLLThreads[] = {128, 256, 512, 1024};
     static const int kLLBlocks[] = {1, 2, 4, 8, 16, 32, 64};
     static const int kHBThreads[] = {128, 256, 512};
     const int hb_blocks[] = {comm->cu_count / 2, comm->cu_count, comm->cu_count * 2};
@@ -555,7 +564,9 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype_arg, int nranks,
         const size_t count = bytes / es > 0 ? bytes / es : 1;
         bytes = count * es;
         // about 200 us of timed work per candidate, between 5 and 20 calls
-        const double est_us = (double)(2 * (size_t)nranks * bytes) / 5.0e3 + 3.0;
+        // (estimate: each rank's message read and written once at 5 TB/s,
+        // plus 3 us)
+        const double est_us = (double)(2 * (size_t)nranks * bytes) / 5.0e6 + 3.0;
         int calls = (int)(200.0 / est_us);
         calls = calls < 5 ? 5 : (calls > 20 ? 20 : calls);
         for (int m = 0; m < 4 && result == arSuccess; ++m) {
@@ -564,18 +575,21 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype_arg, int nranks,
             void *const *dst = in_place ? const_cast<void *const *>(send.data()) : recv.data();
             if (proto == arProtoLL && !ll_possible(comm, nranks, bytes))
                 continue;
-            // LL: each packet width gets the default shape and the grid.  HB:
-            // the same for each access policy (non-temporal first), unless
-            // the communicator's option fixes it.
+            // LL: each packet width (the size's default first) gets the
+            // default shape and the grid.  HB: the same for each access
+            // policy (non-temporal first), unless the communicator's option
+            // fixes it.
             const int nb = proto == arProtoLL ? 7 : 3;
-            const int per_variant = 1 + 3 * nb;
+            const int nth = proto == arProtoLL ? 4 : 3;
+            const int per_variant = 1 + nth * nb;
             const int nt_opt = (int)comm->opt[arOptHBNonTemporal];
             const int variants = proto == arProtoLL ? (comm->ll16_ok ? 2 : 1) : (nt_opt < 0 ? 2 : 1);
             ar::TunedShape best = {0, 0, 0, 0, 0, 0.0f};
             for (int cw = 0; cw < variants * per_variant && result == arSuccess; ++cw) {
                 const int c = cw % per_variant - 1;
                 const int var = cw / per_variant;
-                const int pkt = proto == arProtoLL ? (var == 0 ? 8 : 16) : 0;
+                const int pkt0 = default_ll_packet(comm, nranks, bytes);
+                const int pkt = proto == arProtoLL ? (var == 0 ? pkt0 : 24 - pkt0) : 0;
                 const int nt = proto == arProtoLL ? 0 : (nt_opt >= 0 ? nt_opt : (var == 0 ? 1 : 0));
                 const int th = c < 0 ? 0 : (proto == arProtoLL ? kLLThreads[c / nb] : kHBThreads[c / nb]);
                 const int bl = c < 0 ? 0 : (proto == arProtoLL ? kLLBlocks[c % nb] : hb_blocks[c % nb]);

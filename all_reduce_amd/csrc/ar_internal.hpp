@@ -17,6 +17,38 @@ enum DType { kBf16 = 0, kFp16 = 1, kFp32 = 2 };
 constexpr int kRankVariants = 6;  // 1, 2, 4, 8, 16, 32 -> exact kernels; others -> generic
 constexpr int kThreadChoices = 5; // 64, 128, 256, 512, 1024
 
+// Default LL launch shape for a call that names none and has no tuned entry:
+// threads per workgroup, workgroups per rank and packet width, by rank count
+// (up to 8, 9-16, 17-32) and message size per rank.  Each entry is the
+// fastest of a grid measured on MI355X (bf16, graph-replayed calls; 8- and
+// 16-byte packets, 128-1024 threads, 1-128 workgroups per rank) at a
+// power-of-two size from 2 KiB to 1 MiB per rank, or one within measurement
+// noise of it that is also the best at a neighbouring size.  A size takes
+// the entry of the next power of two up, and sizes above 1 MiB the last one.
+struct LLShape {
+    int threads;
+    int per_rank;
+    int pkt_bytes;
+};
+
+inline LLShape ll_default_shape(int nranks, uint64_t bytes_per_rank)
+{
+    static constexpr LLShape kTable[3][10] = {
+        // 2K          4K          8K          16K          32K          64K
+        // 128K         256K          512K          1M
+        {{256, 1, 8}, {256, 2, 8}, {256, 4, 8}, {256, 8, 8}, {256, 16, 8}, {256, 64, 8},
+         {256, 64, 8}, {128, 64, 16}, {128, 64, 16}, {128, 64, 16}},
+        {{512, 1, 8}, {512, 1, 8}, {512, 2, 8}, {512, 4, 8}, {256, 8, 8}, {256, 32, 8},
+         {256, 32, 8}, {128, 128, 8}, {128, 128, 8}, {128, 64, 8}},
+        {{512, 1, 8}, {512, 1, 8}, {512, 1, 8}, {512, 2, 8}, {512, 4, 8}, {512, 16, 8},
+         {256, 32, 16}, {128, 64, 16}, {256, 8, 16}, {256, 8, 16}},
+    };
+    int s = 0;
+    while (s < 9 && ((uint64_t)2048 << s) < bytes_per_rank)
+        ++s;
+    return kTable[nranks <= 8 ? 0 : (nranks <= 16 ? 1 : 2)][s];
+}
+
 // LL flag schemes (the values of arOptLLFlagScheme): the reader zeroes each
 // consumed packet (the default), or each 512-byte packet group carries a
 // sequence number.

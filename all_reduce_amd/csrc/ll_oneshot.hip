@@ -426,7 +426,6 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
         p.rk.recv[r] = recv[r];
     }
     const uint64_t bytes = (uint64_t)count * T::kBytes;
-    const uint64_t words = (bytes + 3) / 4;
     p.npkt = (bytes + 4 * PW - 1) / (4 * PW);
     p.tail_bytes = (uint32_t)(bytes % (4 * PW));
     p.pkts = comm->pkts;
@@ -443,14 +442,13 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     p.flag_skew = (uint32_t)comm->opt[arOptDebugFlagSkew];
     p.timeout_ticks = (uint64_t)comm->opt[arOptPollTimeoutUs] * comm->wall_clock_khz / 1000u;
 
-    // Default launch shape, measured on MI355X for R = 8 bf16 8-byte packets
-    // from 2 KiB to 1 MiB per rank: 256-thread workgroups (512 from 512 KiB
-    // per rank up), about two words per lane, at most 64 workgroups per rank
-    // (32 from 256 KiB per rank up).  16-byte packets take the same grid, so
-    // each lane moves one packet of two words.
+    // Launch shape: the caller's, else the measured default for the rank
+    // count and size.  With only the workgroup size given, the default's
+    // lanes per rank are kept.
+    const LLShape d = ll_default_shape(nranks, bytes);
     int threads = want_threads;
     if (threads <= 0)
-        threads = words >= 131072 ? 512 : 256;
+        threads = d.threads;
     if (threads > ll_max_threads(RMAX))
         threads = ll_max_threads(RMAX);
     const int resident =
@@ -461,12 +459,9 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
         max_per_rank = 1;
 
     uint64_t per_rank = want_blocks;
-    if (per_rank == 0) {
-        const uint64_t cap = words >= 65536 ? 32 : 64;
-        per_rank = (words + (uint64_t)threads * 2 - 1) / ((uint64_t)threads * 2);
-        if (per_rank > cap)
-            per_rank = cap;
-    }
+    if (per_rank == 0)
+        per_rank = ((uint64_t)d.per_rank * (uint64_t)d.threads + (uint64_t)threads - 1) /
+                   (uint64_t)threads;
     if (per_rank > max_per_rank)
         per_rank = max_per_rank;
     if (per_rank > p.npkt)

@@ -85,7 +85,9 @@ typedef enum {
      * (default 2,000,000).  A wait that runs out records arTimeout in the
      * communicator and the kernel finishes without the missing data. */
     arOptPollTimeoutUs = 0,
-    /* LL: workgroups per simulated rank; 0 = pick from the message size. */
+    /* LL: workgroups per simulated rank; 0 = the built-in default for the
+     * rank count and message size (a table measured on MI355X; with only
+     * arOptLLThreads set, as many lanes per rank as the default has). */
     arOptLLBlocksPerRank = 1,
     /* HB: workgroups in the grid (rounded to a multiple of nranks, capped by
      * the message's tiles); 0 = one per compute unit. */
@@ -103,7 +105,8 @@ typedef enum {
      * capped at 2 above 4 ranks and at 1 above 8); 0 = default (1). */
     arOptHBUnroll = 5,
     /* LL: threads per workgroup (64, 128, 256, 512 or 1024; capped at 512
-     * above 16 ranks); 0 = default. */
+     * above 16 ranks); 0 = the built-in default for the rank count and
+     * message size. */
     arOptLLThreads = 6,
     /* HB: threads per workgroup (64 .. 1024, a multiple of 64; capped at 512
      * above 8 ranks and 256 above 16); 0 = default (256, or 128 from 32 ranks). */
@@ -127,7 +130,9 @@ typedef enum {
     /* LL: packet width in bytes.  8: a 4-byte payload next to a 4-byte flag;
      * 16: two such pairs, written and read as one 16-byte access (half the
      * memory instructions per payload byte).  0 (default): the width the
-     * tuner chose for the message size, else 8.  16 needs the communicator's
+     * tuner chose for the message size, else the built-in default's for the
+     * rank count and size (16 bytes from 256 KiB per rank up to 8 ranks and
+     * from 128 KiB above 16 ranks; 8 bytes otherwise).  16 needs the communicator's
      * packet memory below 4 GiB (maxRanks * maxLLBytesPerRank * 2), else
      * setting it returns arUnsupported. */
     arOptLLPacketBytes = 10,

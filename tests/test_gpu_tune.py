@@ -35,7 +35,7 @@ def test_table_covers_the_tuned_sizes(comm, in_place):
         assert hb[3] == 0 and hb[4] in (0, 1)
         ll = comm.tuned_shape(torch.bfloat16, 8, "ll", 1 << b, in_place)
         if (1 << b) <= comm.max_ll_bytes_per_rank:
-            assert ll is not None and ll[0] in (0, 256, 512, 1024) and ll[2] > 0
+            assert ll is not None and ll[0] in (0, 128, 256, 512, 1024) and ll[2] > 0
             assert ll[3] in (8, 16) and ll[4] == 0
         else:
             assert ll is None, "LL cannot run above maxLLBytesPerRank"
