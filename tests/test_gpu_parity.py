@@ -89,6 +89,21 @@ def test_c5_fp32_integer_sums_full_size(comm, orc, R):
 
 
 # ---- shapes, tails and rank counts --------------------------------------------
+@pytest.mark.parametrize("R", [3, 8, 12, 16, 24, 32])
+@pytest.mark.parametrize("kib", [2, 8, 64, 128, 256, 512, 1024])
+def test_ll_default_shape_table(comm, orc, R, kib):
+    """LL at its built-in default launch shape (no tuning, no shape options) in
+    each rank class of the default table (up to 8, 9-16, 17-32 ranks) and at
+    sizes spanning its columns, including the 16-byte-packet and
+    128-workgroup-per-rank entries; one element short of each power of two,
+    so every size ends in a partial packet or vector."""
+    N = kib * 512 - 1
+    x = inputs.make(R, N, "bf16", "normal", seed=3000 + R * 7 + kib)
+    check(comm, orc, x, "ll", what=f"ll default shape R={R} {kib} KiB")
+    check(comm, orc, x, "ll", inplace=True, what=f"ll default shape in place R={R} {kib} KiB")
+
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8, 13, 16, 24, 32])
 @pytest.mark.parametrize("N", [1, 2, 3, 7, 9, 1023, 1025, 65536 + 5])
