@@ -308,6 +308,24 @@ class Comm:
 
         ``protocol`` is "ll", "hb" or "auto" (the tuned faster one; HB where
         nothing was tuned)."""
+        send, recv = self._check_ranks(send, recv)
+        t0 = send[0]
+        r = arAllReduce([t.data_ptr() for t in send], [t.data_ptr() for t in recv],
+                        t0.numel(), dtype_code(t0.dtype), arRedOp.arSum, len(send),
+                        protocol_code(protocol), self.handle, self._stream(stream))
+        if r != 0:
+            raise ArError(r, "arAllReduce")
+        return recv
+
+    def prepare(self, send, recv=None, protocol="auto", stream=None) -> "PreparedAllReduce":
+        """``all_reduce(send, recv, protocol, stream)`` with its arguments
+        marshalled once, for a loop that reduces the same buffers again and
+        again without a graph.  The stream is fixed here (default: the current
+        stream now); the tensors are kept alive by the returned call."""
+        send, recv = self._check_ranks(send, recv)
+        return PreparedAllReduce(self, send, recv, protocol_code(protocol), self._stream(stream))
+
+    def _check_ranks(self, send, recv):
         if recv is None:
             recv = send
         if len(send) != len(recv) or not send:
@@ -320,9 +338,27 @@ class Comm:
                 raise ValueError("all rank tensors need the same dtype and size")
             if not t.is_contiguous():
                 raise ValueError("rank tensors must be contiguous")
-        r = arAllReduce([t.data_ptr() for t in send], [t.data_ptr() for t in recv],
-                        t0.numel(), dtype_code(t0.dtype), arRedOp.arSum, len(send),
-                        protocol_code(protocol), self.handle, self._stream(stream))
+        return list(send), list(recv)
+
+
+class PreparedAllReduce:
+    """One ``arAllReduce`` call whose arguments (pointer arrays, count, dtype,
+    protocol, communicator, stream) were marshalled once: calling it is a
+    single foreign call.  Made by ``Comm.prepare``."""
+
+    __slots__ = ("_fn", "_args", "_keep")
+
+    def __init__(self, comm, send, recv, protocol, stream):
+        n = len(send)
+        t0 = send[0]
+        self._fn = library().arAllReduce
+        self._args = (_pointer_array([t.data_ptr() for t in send], n),
+                      _pointer_array([t.data_ptr() for t in recv], n),
+                      t0.numel(), int(dtype_code(t0.dtype)), int(arRedOp.arSum), n,
+                      int(protocol), comm.handle, stream)
+        self._keep = (comm, send, recv)
+
+    def __call__(self):
+        r = self._fn(*self._args)
         if r != 0:
             raise ArError(r, "arAllReduce")
-        return recv

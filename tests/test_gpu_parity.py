@@ -88,6 +88,46 @@ def test_c5_fp32_integer_sums_full_size(comm, orc, R):
     assert_parity(got[:, idx].contiguous(), want, f"C5 fp32 R={R} sampled")
 
 
+# ---- the prepared call ---------------------------------------------------------
+@pytest.mark.parametrize("protocol", ["ll", "hb", "auto"])
+def test_prepared_call(comm, orc, protocol):
+    """Comm.prepare marshals the arguments once; every call of the result is a
+    full all-reduce: new inputs give new sums, out of place and in place."""
+    R, N = 8, 10_007
+    _, sv = ar.rank_buffers(R, N, torch.bfloat16, comm.device)
+    plane, rv = ar.rank_buffers(R, N, torch.bfloat16, comm.device)
+    out_of_place = comm.prepare(sv, rv, protocol)
+    in_place = comm.prepare(sv, None, protocol)
+    for seed in (51, 52):
+        x = inputs.make(R, N, "bf16", "normal", seed=seed)
+        want = expect(orc, x)
+        for r in range(R):
+            sv[r].copy_(x[r])
+        plane.view(torch.uint8).fill_(0xA5)
+        note(f"prepared {protocol} out of place, seed {seed}")
+        out_of_place()
+        torch.cuda.synchronize()
+        assert_parity(torch.stack([t.cpu() for t in rv]), want, f"prepared {protocol} seed {seed}")
+        note(f"prepared {protocol} in place, seed {seed}")
+        in_place()
+        torch.cuda.synchronize()
+        assert_parity(torch.stack([t.cpu() for t in sv]), want,
+                      f"prepared {protocol} in place seed {seed}")
+
+
+def test_prepared_call_reports_errors(comm):
+    """A prepared call raises the library's error like all_reduce does (here:
+    LL above the communicator's LL size limit)."""
+    R, N = 2, (2 << 20) // 2
+    _, sv = ar.rank_buffers(R, N, torch.bfloat16, comm.device)
+    call = comm.prepare(sv, None, "ll")
+    with pytest.raises(ar.ArError) as err:
+        call()
+    assert err.value.code == ar.arResult.arInvalidUsage
+    with pytest.raises(ValueError):
+        comm.prepare(sv, sv[:1], "hb")
+
+
 # ---- shapes, tails and rank counts --------------------------------------------
 @pytest.mark.parametrize("R", [3, 8, 12, 16, 24, 32])
 @pytest.mark.parametrize("kib", [2, 8, 64, 128, 256, 512, 1024])
