@@ -60,6 +60,7 @@ class arOption(IntEnum):
     arOptHBStaged = 11
     arOptLLFlagScheme = 12
     arOptDebugSeqStart = 13
+    arOptTuneFreshInputs = 14
 
 
 AR_MAX_RANKS = 32

@@ -74,7 +74,7 @@ constexpr int ll_kind(bool seq, int node)
 
 }  // namespace ar
 
-constexpr int kOptionCount = 14;
+constexpr int kOptionCount = 15;
 
 namespace ar {
 // One tuned launch shape: threads per workgroup and workgroups (HB: the

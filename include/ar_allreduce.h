@@ -160,7 +160,15 @@ typedef enum {
     /* Test hook: the value arCommReset writes to every sequence-table entry
      * (0 .. 0xFFFFFFFF; default 0), to exercise the sequence numbers' wrap.
      * Takes effect at the next arCommReset. */
-    arOptDebugSeqStart = 13
+    arOptDebugSeqStart = 13,
+    /* arCommTune's timing method.  0 (default): each candidate replays on
+     * unchanged inputs, which stay in the last-level cache between calls, as
+     * the benchmark's graph replays do.  1: before each timed call a copy-like
+     * kernel rewrites the inputs (every 16-byte vector of each rank's
+     * message), as when every step of a model produces new inputs; the
+     * rewrites' own time, measured alone, is subtracted.  On MI355X this
+     * changes the HB access policy that wins from a few MiB per rank up. */
+    arOptTuneFreshInputs = 14
 } arOption_t;
 
 /* Create a communicator on `device` for groups of up to `maxRanks` (1..32)
@@ -221,7 +229,8 @@ arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
  * Each candidate is timed the way latency-sensitive callers run the library:
  * its calls captured into a HIP graph on a private stream of the tuner, and
  * the graph replayed (eager launches would time the host's launch rate at
- * small sizes).  Allocates two scratch planes of nranks * maxBytesPerRank
+ * small sizes); with arOptTuneFreshInputs = 1, each call right after a
+ * rewrite of its inputs, the rewrites' time subtracted.  Allocates two scratch planes of nranks * maxBytesPerRank
  * bytes for the duration, waits for `stream` first and synchronises the
  * device at the end: never call it while a stream is being captured.
  * Returns arInvalidArgument for a NULL comm or maxBytesPerRank outside

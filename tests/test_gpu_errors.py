@@ -71,6 +71,12 @@ def test_option_ranges(comm):
     for bad in (-2, 2):
         with pytest.raises(ar.ArError):
             comm.set_option(ar.arOption.arOptHBNonTemporal, bad)
+    # tuning method: 0 (unchanged inputs, the default) or 1 (fresh inputs)
+    with ar.Comm(device="cuda:0", max_ranks=2, max_ll_bytes_per_rank=0) as fresh:
+        assert fresh.get_option(ar.arOption.arOptTuneFreshInputs) == 0
+    for bad in (-1, 2):
+        with pytest.raises(ar.ArError):
+            comm.set_option(ar.arOption.arOptTuneFreshInputs, bad)
 
 
 def test_two_communicators_on_two_streams_at_once(orc):

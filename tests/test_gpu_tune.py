@@ -103,3 +103,33 @@ def test_tuning_up_to_a_size_that_is_no_power_of_two(orc):
             x = inputs.make(4, n, "fp16", "normal", seed=80 + n)
             for proto in ("ll", "hb", "auto"):
                 assert_parity(run_allreduce(c, x, proto), expect(orc, x), f"{proto} N={n}")
+
+
+def test_tuning_on_fresh_inputs(orc):
+    """arOptTuneFreshInputs = 1: each candidate is timed after a rewrite of its
+    inputs, the rewrites' time subtracted.  The table covers every size and
+    mode with positive times, calls keep their bits, and the tuner leaves the
+    caller's buffers alone (it rewrites only its own scratch planes)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    with ar.Comm(device="cuda:0", max_ranks=8, max_ll_bytes_per_rank=1 << 18) as c:
+        x = inputs.make(8, 70_001, "bf16", "normal", seed=91)
+        want = expect(orc, x)
+        _, sv = ar.rank_buffers(8, x.shape[1], torch.bfloat16, c.device)
+        for r in range(8):
+            sv[r].copy_(x[r])
+        c.set_option(ar.arOption.arOptTuneFreshInputs, 1)
+        note("arCommTune bf16 R=8 up to 4 MiB, fresh inputs")
+        c.tune(torch.bfloat16, 8, 4 << 20)
+        assert torch.equal(torch.stack([t.cpu() for t in sv]), x), "tuning touched caller data"
+        for in_place in (False, True):
+            for b in range(9, 23):
+                hb = c.tuned_shape(torch.bfloat16, 8, "hb", 1 << b, in_place)
+                assert hb is not None and hb[2] > 0 and hb[4] in (0, 1)
+                ll = c.tuned_shape(torch.bfloat16, 8, "ll", 1 << b, in_place)
+                assert (ll is not None and ll[2] > 0) == ((1 << b) <= (1 << 18))
+        for proto in ("ll", "hb", "auto"):
+            for in_place in (False, True):
+                assert_parity(run_allreduce(c, x, proto, inplace=in_place), want,
+                              f"fresh-tuned {proto} in_place={in_place}")
+        assert c.async_error() == ar.arResult.arSuccess
