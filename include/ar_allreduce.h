@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define AR_VERSION 10100 /* 1.1.0 */
+#define AR_VERSION 10200 /* 1.2.0 */
 #define AR_MAX_RANKS 32
 
 typedef struct arComm *arComm_t;
