@@ -589,8 +589,8 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype_arg, int nranks,
         recv[(size_t)r] = rplane + (size_t)r * stride;
     }
 
-    // Candidate shapes: the built-in default first, then the (threads per
-    // workgroup, workgroups) grid it was chosen from.  The launchers clamp each
+    // Candidate shapes: the built-in default first, then a (threads per
+    // workgroup, workgroups) grid around it.  The launchers clamp each
     // to what the kernel and the message allow.  A candidate replaces the best
     // so far only if it is more than 3 % faster, so timing noise does not move
     // the choice away from the default.
