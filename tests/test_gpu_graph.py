@@ -175,3 +175,42 @@ def test_reset_captured_in_a_graph(comm, orc, scheme):
         assert comm.async_error() == ar.arResult.arSuccess
     finally:
         comm.set_option(ar.arOption.arOptLLFlagScheme, 0)
+
+
+@pytest.mark.parametrize("protocol", ["ll", "hb"])
+def test_prepared_calls_captured(comm, orc, protocol):
+    """Calls made with Comm.prepare inside the capture (so they are bound to the
+    capturing stream) replay like direct calls: each replay, with new inputs
+    copied in between, matches the oracle."""
+    R, N, dt = 8, 40_003, "bf16"
+    plane, sv = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    _, rv = ar.rank_buffers(R, N, torch.bfloat16, "cuda")
+    x0 = inputs.make(R, N, dt, "normal", seed=4300)
+    for r in range(R):
+        sv[r].copy_(x0[r])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        warm = comm.prepare(sv, rv, protocol)
+        warm()
+        warm()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    note(f"prepared {protocol}: capture 3 calls")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step = comm.prepare(sv, rv, protocol)
+        for _ in range(3):
+            step()
+    for i in range(3):
+        x = inputs.make(R, N, dt, "normal", seed=4301 + i)
+        for r in range(R):
+            sv[r].copy_(x[r])
+        rv[0].zero_()
+        torch.cuda.synchronize()
+        note(f"prepared {protocol}: replay {i}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert_parity(torch.stack([t.cpu() for t in rv]), expect(orc, x),
+                      f"prepared {protocol} replay {i}")
+    assert comm.async_error() == ar.arResult.arSuccess
