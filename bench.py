@@ -14,8 +14,9 @@ Default run (inputs resident in HBM before every timed region):
   10 calls captured in one graph, ``--warmup`` untimed replays, then
   ``--steps`` replays inside one HIP event pair; latency per call = elapsed /
   (steps * 10).  Each size also gets the guide's eager timing (2 warm-up calls,
-  then the mean of 10 back-to-back calls) for LL and HB, and a timing-only
-  plain-torch row (stack, fp32 sum, cast, copy to every rank).
+  then the mean of 10 back-to-back calls) for LL and HB, through prepared
+  calls (arguments marshalled once), and a timing-only plain-torch row (stack,
+  fp32 sum, cast, copy to every rank).
 * LL vs HB at the decode shape 64 x 8192 with N(0, 1) values.
 * HB prefill -- R = 8 bf16, 8192 x 8192 elements per rank (128 MiB), N(0, 1)
   with 0.1 % of entries x1000, in place.  The roofline figure uses ``--steps``
