@@ -73,6 +73,14 @@ class arTunedShape(ctypes.Structure):
                 ("us", ctypes.c_float)]
 
 
+class arLaunchInfo(ctypes.Structure):
+    """Mirror of arLaunchInfo_t."""
+    _fields_ = [("protocol", ctypes.c_int), ("kernels", ctypes.c_int), ("grid", ctypes.c_uint),
+                ("threads", ctypes.c_uint), ("packetBytes", ctypes.c_int),
+                ("nonTemporal", ctypes.c_int), ("nodeRanks", ctypes.c_int),
+                ("staged", ctypes.c_int)]
+
+
 class ArError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = arResult(code)
@@ -101,6 +109,8 @@ def library() -> ctypes.CDLL:
         "arAllReduce": ([ctypes.POINTER(vp), ctypes.POINTER(vp), sz, i32, i32, i32, i32, vp, vp], i32),
         "arCommTune": ([vp, i32, i32, sz, vp], i32),
         "arCommGetTunedShape": ([vp, i32, i32, i32, sz, i32, ctypes.POINTER(arTunedShape)], i32),
+        "arCommGetLastLaunch": ([vp, ctypes.POINTER(arLaunchInfo)], i32),
+        "arCommSetWorkspace": ([vp, vp, sz], i32),
         "arGetErrorString": ([i32], ctypes.c_char_p),
         "arGetVersion": ([], i32),
     }
@@ -166,6 +176,18 @@ def arCommGetTunedShape(comm, dtype: int, nranks: int, protocol: int, bytes_per_
     return r, shape
 
 
+def arCommSetWorkspace(comm, workspace, nbytes: int) -> int:
+    """``workspace`` a device pointer as an integer, or None with 0."""
+    return library().arCommSetWorkspace(comm, workspace, nbytes)
+
+
+def arCommGetLastLaunch(comm):
+    """Returns (result code, arLaunchInfo)."""
+    info = arLaunchInfo()
+    r = library().arCommGetLastLaunch(comm, ctypes.byref(info))
+    return r, info
+
+
 def _pointer_array(ptrs: Sequence[int] | None, nranks: int):
     """ctypes array of device pointers, NULL-padded to ``nranks`` entries so the
     library never reads past it (it rejects nranks > AR_MAX_RANKS before reading
@@ -226,16 +248,21 @@ class Comm:
     def __init__(self, device=None, max_ranks: int = AR_MAX_RANKS,
                  max_ll_bytes_per_rank: int = 1 << 20):
         torch = _torch()
-        dev = torch.device("cuda", torch.cuda.current_device()) if device is None \
-            else torch.device(device)
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        if dev.type != "cuda":
+            raise ValueError(f"a communicator needs a GPU device, not {dev}")
+        # "cuda" without an index means the current device; resolve it now, so
+        # that tensors on "cuda:<i>" compare equal to the communicator's device.
+        dev = torch.device("cuda", dev.index if dev.index is not None
+                           else torch.cuda.current_device())
         self.device = dev
-        r, h = arCommCreate(dev.index if dev.index is not None else 0, max_ranks,
-                            max_ll_bytes_per_rank)
+        r, h = arCommCreate(dev.index, max_ranks, max_ll_bytes_per_rank)
         if r != 0:
             raise ArError(r, "arCommCreate")
         self.handle = h
         self.max_ranks = max_ranks
         self.max_ll_bytes_per_rank = max_ll_bytes_per_rank
+        self._workspace = None
 
     def close(self):
         """Free the communicator after the device has finished the work using it."""
@@ -293,6 +320,32 @@ class Comm:
             raise ArError(r, "arCommGetTunedShape")
         return None if s.tuned == 0 else (s.threads, s.blocks, s.us, s.packetBytes, s.nonTemporal)
 
+    def set_workspace(self, workspace):
+        """Attach a device tensor (256-byte aligned, on the communicator's
+        device) as the staged two-level form's workspace, or None to detach.
+        The tensor is kept alive while attached."""
+        if workspace is None:
+            r = arCommSetWorkspace(self.handle, None, 0)
+        else:
+            if not workspace.is_contiguous() or workspace.device != self.device:
+                raise ValueError("the workspace must be a contiguous tensor on the "
+                                 "communicator's device")
+            r = arCommSetWorkspace(self.handle, workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size())
+        if r != 0:
+            raise ArError(r, "arCommSetWorkspace")
+        self._workspace = workspace
+
+    def last_launch(self) -> dict | None:
+        """The shape of the communicator's most recent launch (see
+        arCommGetLastLaunch) as a dict, or None before the first one."""
+        r, info = arCommGetLastLaunch(self.handle)
+        if r != 0:
+            raise ArError(r, "arCommGetLastLaunch")
+        if info.protocol < 0:
+            return None
+        return {name: getattr(info, name) for name, _ in info._fields_}
+
     def reset(self, stream=None):
         r = arCommReset(self.handle, self._stream(stream))
         if r != 0:
@@ -344,22 +397,29 @@ class Comm:
 
 class PreparedAllReduce:
     """One ``arAllReduce`` call whose arguments (pointer arrays, count, dtype,
-    protocol, communicator, stream) were marshalled once: calling it is a
-    single foreign call.  Made by ``Comm.prepare``."""
+    protocol, stream) were marshalled once: calling it is a single foreign
+    call.  Made by ``Comm.prepare``.  The communicator's handle is read at each
+    call, so a call after ``Comm.close()`` raises instead of passing a freed
+    communicator to the library."""
 
-    __slots__ = ("_fn", "_args", "_keep")
+    __slots__ = ("_fn", "_head", "_tail", "_comm", "_keep")
 
     def __init__(self, comm, send, recv, protocol, stream):
         n = len(send)
         t0 = send[0]
         self._fn = library().arAllReduce
-        self._args = (_pointer_array([t.data_ptr() for t in send], n),
+        self._head = (_pointer_array([t.data_ptr() for t in send], n),
                       _pointer_array([t.data_ptr() for t in recv], n),
                       t0.numel(), int(dtype_code(t0.dtype)), int(arRedOp.arSum), n,
-                      int(protocol), comm.handle, stream)
-        self._keep = (comm, send, recv)
+                      int(protocol))
+        self._tail = stream
+        self._comm = comm
+        self._keep = (send, recv)
 
     def __call__(self):
-        r = self._fn(*self._args)
+        h = self._comm.handle
+        if h is None:
+            raise ValueError("the communicator of this prepared call was closed")
+        r = self._fn(*self._head, h, self._tail)
         if r != 0:
             raise ArError(r, "arAllReduce")

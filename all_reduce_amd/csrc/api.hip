@@ -63,6 +63,12 @@ bool overlaps(uintptr_t a, uintptr_t b, size_t len)
     return a < b + len && b < a + len;
 }
 
+// [a, a + la) and [b, b + lb) share a byte.
+bool ranges_overlap(uintptr_t a, size_t la, uintptr_t b, size_t lb)
+{
+    return a < b + lb && b < a + la;
+}
+
 constexpr int64_t kDefaults[kOptionCount] = {
     2000000,  // arOptPollTimeoutUs
     0,        // arOptLLBlocksPerRank (auto)
@@ -156,6 +162,14 @@ arProtocol_t resolve_protocol(const arComm *comm, arDataType_t dtype, int nranks
     return arProtoHB;
 }
 
+// The HB launchers' view of a communicator: its compute units and HB
+// options, and its launch record.
+ar::HBConfig hb_config(const arComm *comm)
+{
+    return {comm->cu_count, (int)comm->opt[arOptHBUnroll], comm->opt[arOptHBChunkLayout] == 1,
+            &comm->last};
+}
+
 hipError_t launch(const void *const *send, void *const *recv, size_t count, arDataType_t dtype,
                   int nranks, arProtocol_t proto, const arComm *comm, int threads,
                   uint64_t blocks, int pkt_bytes, int scheme, int group, bool nt,
@@ -164,8 +178,8 @@ hipError_t launch(const void *const *send, void *const *recv, size_t count, arDa
     return proto == arProtoLL
                ? ar::launch_ll(send, recv, count, (int)dtype, nranks, comm, threads, blocks,
                                pkt_bytes, scheme, group, stream)
-               : ar::launch_hb(send, recv, count, (int)dtype, nranks, comm, threads, blocks, group,
-                               nt, stream);
+               : ar::launch_hb(send, recv, count, (int)dtype, nranks, hb_config(comm), threads,
+                               blocks, group, nt, stream);
 }
 
 // The tuner's input rewrite (arOptTuneFreshInputs): the first `vecs` 16-byte
@@ -257,13 +271,6 @@ hipError_t time_candidate(const void *const *send, void *const *dst, size_t coun
     return e;
 }
 
-// Default LL packet width: the measured default shape's, when the
-// communicator allows 16-byte packets.
-int default_ll_packet(const arComm *comm, int nranks, size_t bytes_per_rank)
-{
-    return comm->ll16_ok && ar::ll_default_shape(nranks, bytes_per_rank).pkt_bytes == 16 ? 16 : 8;
-}
-
 // Ranks per simulated node when a hierarchical order is in force, else 0.
 int hierarchy_group(const arComm *comm, int nranks)
 {
@@ -332,6 +339,9 @@ arResult_t arCommCreate(arComm_t *comm, int device, int maxRanks, size_t maxLLBy
     c->max_ranks = maxRanks;
     c->max_ll_bytes = maxLLBytesPerRank;
     memcpy(c->opt, kDefaults, sizeof(kDefaults));
+    c->last = {-1, 0, 0, 0, 0, 0, 0, 0};
+    c->ws = nullptr;
+    c->ws_bytes = 0;
 
     int cus = 0, clock_khz = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
@@ -457,6 +467,21 @@ arResult_t arCommSetOption(arComm_t comm, arOption_t option_arg, int64_t value)
     return arSuccess;
 }
 
+arResult_t arCommSetWorkspace(arComm_t comm, void *workspace, size_t bytes)
+{
+    if (comm == nullptr)
+        return reject(arInvalidArgument, "NULL comm");
+    if ((workspace == nullptr) != (bytes == 0))
+        return reject(arInvalidArgument, "a workspace needs both a pointer and a size");
+    if (((uintptr_t)workspace & 255u) != 0)
+        return reject(arInvalidArgument, "the workspace must be 256-byte aligned");
+    if (workspace != nullptr && (uintptr_t)workspace > UINTPTR_MAX - bytes)
+        return reject(arInvalidArgument, "the workspace wraps the address space");
+    comm->ws = workspace;
+    comm->ws_bytes = bytes;
+    return arSuccess;
+}
+
 arResult_t arCommGetOption(arComm_t comm, arOption_t option_arg, int64_t *value)
 {
     if (comm == nullptr || value == nullptr)
@@ -487,16 +512,28 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
         in_place &= sendbufs[r] == recvbufs[r] ? 1 : 0;
     if (group != 0 && nranks % group != 0)
         return reject(arInvalidUsage, "nranks is not a multiple of arOptNodeRanks");
-    // The hierarchical order is built into the fused HB kernel and the LL
-    // kernel of the cleared flag scheme; the two ablations keep the flat order.
+    // The hierarchical order is built into the fused HB kernel, the LL kernel
+    // of the cleared flag scheme and the staged two-level HB form; the
+    // sequenced LL ablation keeps the flat order.
     const bool staged = comm->opt[arOptHBStaged] != 0;
     const bool seq_ll = comm->opt[arOptLLFlagScheme] == ar::kSchemeSequenced;
     const arProtocol_t proto = resolve_protocol(comm, dtype, nranks, bytes, in_place, protocol,
                                                 group == 0 || !seq_ll);
     if (group != 0 && proto == arProtoLL && seq_ll)
         return reject(arUnsupported, "the sequenced LL scheme sums in the flat order only");
-    if (group != 0 && proto == arProtoHB && staged)
-        return reject(arUnsupported, "the staged HB form sums in the flat order only");
+    const bool two_level = group != 0 && proto == arProtoHB && staged;
+    if (two_level) {
+        const uint64_t need = ar::hier_workspace_bytes(count, nranks / group);
+        if (comm->ws == nullptr || comm->ws_bytes < need)
+            return reject(arInvalidUsage, "the staged two-level form needs a workspace of "
+                                          "(nranks / arOptNodeRanks) * roundup(count * 4, 256) "
+                                          "bytes (arCommSetWorkspace)");
+        const uintptr_t w = (uintptr_t)comm->ws;
+        for (int r = 0; r < nranks; ++r)
+            if (ranges_overlap(w, need, (uintptr_t)sendbufs[r], bytes) ||
+                ranges_overlap(w, need, (uintptr_t)recvbufs[r], bytes))
+                return reject(arInvalidArgument, "the workspace overlaps a rank buffer");
+    }
     if (proto == arProtoLL) {
         if (nranks > comm->max_ranks)
             return reject(arInvalidUsage, "nranks above the communicator's maxRanks");
@@ -530,18 +567,24 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
     }
     if (nt < 0)
         nt = 1;
-    if (pkt == 0)
-        pkt = default_ll_packet(comm, nranks, bytes);
+    // 8-byte packets unless the caller asked for 16 (an ablation: the 16-byte
+    // packet relies on each 8-byte half of a 128-bit store becoming visible as
+    // a unit, which no document guarantees).
     if (pkt != 16 || !comm->ll16_ok)
         pkt = 8;
-    // The staged HB form is an ablation: explicit options or its defaults,
-    // never the fused kernel's tuned shape.
+    // The staged HB forms take explicit options or their defaults, never the
+    // fused kernel's tuned shape.
+    const ar::HBConfig cfg = hb_config(comm);
+    const int st_threads = (int)comm->opt[arOptHBThreads];
+    const uint64_t st_blocks = (uint64_t)comm->opt[arOptHBBlocks];
+    const bool st_nt = comm->opt[arOptHBNonTemporal] != 0;
     const hipError_t e =
-        proto == arProtoHB && staged
-            ? ar::launch_hb_staged(sendbufs, recvbufs, count, (int)dtype, nranks, comm,
-                                   (int)comm->opt[arOptHBThreads],
-                                   (uint64_t)comm->opt[arOptHBBlocks],
-                                   comm->opt[arOptHBNonTemporal] != 0, (hipStream_t)stream)
+        two_level ? ar::launch_hb_hier(sendbufs, recvbufs, count, (int)dtype, nranks, group,
+                                       comm->ws, cfg, st_threads, st_blocks, st_nt,
+                                       (hipStream_t)stream)
+        : proto == arProtoHB && staged
+            ? ar::launch_hb_staged(sendbufs, recvbufs, count, (int)dtype, nranks, cfg, st_threads,
+                                   st_blocks, st_nt, (hipStream_t)stream)
             : launch(sendbufs, recvbufs, count, dtype, nranks, proto, comm, threads, blocks, pkt,
                      scheme, group, nt != 0, (hipStream_t)stream);
     if (e != hipSuccess)
@@ -616,15 +659,15 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype_arg, int nranks,
             void *const *dst = in_place ? const_cast<void *const *>(send.data()) : recv.data();
             if (proto == arProtoLL && !ll_possible(comm, nranks, bytes))
                 continue;
-            // LL: each packet width (the size's default first) gets the
-            // default shape and the grid.  HB: the same for each access
-            // policy (non-temporal first), unless the communicator's option
-            // fixes it.
+            // LL: the default shape and the grid, with 8-byte packets (the
+            // 16-byte packet is an ablation a caller must ask for).  HB: the
+            // same for each access policy (non-temporal first), unless the
+            // communicator's option fixes it.
             const int nb = proto == arProtoLL ? 7 : 3;
             const int nth = proto == arProtoLL ? 4 : 3;
             const int per_variant = 1 + nth * nb;
             const int nt_opt = (int)comm->opt[arOptHBNonTemporal];
-            const int variants = proto == arProtoLL ? (comm->ll16_ok ? 2 : 1) : (nt_opt < 0 ? 2 : 1);
+            const int variants = proto == arProtoLL ? 1 : (nt_opt < 0 ? 2 : 1);
             // Fresh inputs: the rewrites alone are timed first, and each
             // candidate's time is its graph's time less theirs.
             const TuneFill fill = {fresh ? splane : nullptr, stride, bytes / 16, nranks};
@@ -643,8 +686,7 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype_arg, int nranks,
             for (int cw = 0; cw < variants * per_variant && result == arSuccess; ++cw) {
                 const int c = cw % per_variant - 1;
                 const int var = cw / per_variant;
-                const int pkt0 = default_ll_packet(comm, nranks, bytes);
-                const int pkt = proto == arProtoLL ? (var == 0 ? pkt0 : 24 - pkt0) : 0;
+                const int pkt = proto == arProtoLL ? 8 : 0;
                 const int nt = proto == arProtoLL ? 0 : (nt_opt >= 0 ? nt_opt : (var == 0 ? 1 : 0));
                 const int th = c < 0 ? 0 : (proto == arProtoLL ? kLLThreads[c / nb] : kHBThreads[c / nb]);
                 const int bl = c < 0 ? 0 : (proto == arProtoLL ? kLLBlocks[c % nb] : hb_blocks[c % nb]);
@@ -684,6 +726,22 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype_arg, int nranks,
             result = reject(arTimeout, "an LL wait timed out while tuning");
     }
     return result;
+}
+
+arResult_t arCommGetLastLaunch(arComm_t comm, arLaunchInfo_t *info)
+{
+    if (comm == nullptr || info == nullptr)
+        return reject(arInvalidArgument, "NULL argument");
+    const ar::LaunchRecord &l = comm->last;
+    info->protocol = l.protocol;
+    info->kernels = l.kernels;
+    info->grid = l.grid;
+    info->threads = l.threads;
+    info->packetBytes = l.pkt_bytes;
+    info->nonTemporal = l.nt;
+    info->nodeRanks = l.node;
+    info->staged = l.staged;
+    return arSuccess;
 }
 
 arResult_t arCommGetTunedShape(arComm_t comm, arDataType_t dtype_arg, int nranks,

@@ -18,30 +18,29 @@ constexpr int kRankVariants = 6;  // 1, 2, 4, 8, 16, 32 -> exact kernels; others
 constexpr int kThreadChoices = 5; // 64, 128, 256, 512, 1024
 
 // Default LL launch shape for a call that names none and has no tuned entry:
-// threads per workgroup, workgroups per rank and packet width, by rank count
-// (up to 8, 9-16, 17-32) and message size per rank.  Each entry is the
-// fastest of a grid measured on MI355X (bf16, graph-replayed calls; 8- and
-// 16-byte packets, 128-1024 threads, 1-128 workgroups per rank) at a
-// power-of-two size from 2 KiB to 1 MiB per rank, or one within measurement
-// noise of it that is also the best at a neighbouring size.  A size takes
-// the entry of the next power of two up, and sizes above 1 MiB the last one.
+// threads per workgroup and workgroups per rank, by rank count (up to 8,
+// 9-16, 17-32) and message size per rank, for 8-byte packets.  Each entry is
+// the fastest of a grid measured on MI355X (bf16, graph-replayed calls,
+// 64-1024 threads, 1-128 workgroups per rank) at a power-of-two size from
+// 2 KiB to 1 MiB per rank, or one within measurement noise of it that is also
+// the best at a neighbouring size.  A size takes the entry of the next power
+// of two up, and sizes above 1 MiB the last one.
 struct LLShape {
     int threads;
     int per_rank;
-    int pkt_bytes;
 };
 
 inline LLShape ll_default_shape(int nranks, uint64_t bytes_per_rank)
 {
     static constexpr LLShape kTable[3][10] = {
-        // 2K          4K          8K          16K          32K          64K
-        // 128K         256K          512K          1M
-        {{256, 1, 8}, {256, 2, 8}, {256, 4, 8}, {256, 8, 8}, {256, 16, 8}, {256, 64, 8},
-         {256, 64, 8}, {128, 64, 16}, {128, 64, 16}, {128, 64, 16}},
-        {{512, 1, 8}, {512, 1, 8}, {512, 2, 8}, {512, 4, 8}, {256, 8, 8}, {256, 32, 8},
-         {256, 32, 8}, {128, 128, 8}, {128, 128, 8}, {128, 64, 8}},
-        {{512, 1, 8}, {512, 1, 8}, {512, 1, 8}, {512, 2, 8}, {512, 4, 8}, {512, 16, 8},
-         {256, 32, 16}, {128, 64, 16}, {256, 8, 16}, {256, 8, 16}},
+        // 2K        4K        8K        16K       32K        64K
+        // 128K      256K       512K       1M
+        {{256, 1}, {256, 2}, {256, 4}, {256, 8}, {256, 16}, {256, 64},
+         {256, 64}, {256, 32}, {512, 32}, {512, 32}},
+        {{512, 1}, {512, 1}, {512, 2}, {512, 4}, {256, 8}, {256, 32},
+         {256, 32}, {128, 128}, {512, 16}, {512, 16}},
+        {{512, 1}, {512, 1}, {512, 1}, {512, 2}, {512, 4}, {512, 16},
+         {256, 16}, {128, 32}, {512, 8}, {512, 8}},
     };
     int s = 0;
     while (s < 9 && ((uint64_t)2048 << s) < bytes_per_rank)
@@ -84,12 +83,24 @@ struct TunedShape {
     int32_t valid;
     int32_t threads;
     int32_t blocks;
-    int32_t pkt_bytes;  // LL packet width that won: 8 or 16 (HB: 0)
+    int32_t pkt_bytes;  // LL packet width it was timed with: 8 (HB: 0)
     int32_t nt;         // HB: non-temporal (1) or cached (0) accesses won (LL: 0)
     float us;
 };
 // Message sizes are bucketed by ceil(log2(bytes per rank)).
 constexpr int kBuckets = 41;
+
+// What the communicator's most recent launch was (arCommGetLastLaunch).
+struct LaunchRecord {
+    int32_t protocol;   // arProtoLL or arProtoHB; -1 before the first launch
+    int32_t kernels;    // kernels enqueued by the call
+    uint32_t grid;      // workgroups of the (first) kernel
+    uint32_t threads;   // threads per workgroup
+    int32_t pkt_bytes;  // LL packet width (HB: 0)
+    int32_t nt;         // HB: non-temporal accesses (LL: 0)
+    int32_t node;       // ranks per node of a hierarchical order, else 0
+    int32_t staged;     // HB: 1 for a staged form (kernel boundary between shots)
+};
 }  // namespace ar
 
 struct arComm {
@@ -113,9 +124,27 @@ struct arComm {
     // shapes (8 x 128 MiB bf16: 256 x 256 is fastest in place, 512 workgroups
     // out of place, each about 10 % off on the other).
     ar::TunedShape tuned[3][AR_MAX_RANKS + 1][2][2][ar::kBuckets];
+    // Written by the launchers (which see the communicator as const): the
+    // shape of the most recent launch, for arCommGetLastLaunch.
+    mutable ar::LaunchRecord last;
+    // Caller-owned device memory for the staged two-level HB form's node
+    // partials (arCommSetWorkspace); nullptr: none.
+    void *ws;
+    size_t ws_bytes;
 };
 
 namespace ar {
+
+// What the HB launchers need besides the call's arguments: the chip's compute
+// units (the default grid), the vectors per lane and the chunk layout, and
+// where to record the launch (may be null).  Built from a communicator's
+// options, or from the defaults by the entry point that has none.
+struct HBConfig {
+    int cu_count;
+    int unroll;          // 16-byte vectors per lane per rank (0: 1)
+    bool interleaved;    // chunk c = every R-th tile (else contiguous N/R)
+    LaunchRecord *rec;
+};
 
 // Launchers: validate nothing (the ABI layer did), pick the instantiation,
 // enqueue on `stream`.  `threads` and `blocks` give the launch shape (HB: the
@@ -127,7 +156,7 @@ namespace ar {
 // 1 < group < nranks and nranks % group == 0.  `nt` selects non-temporal
 // loads and stores (else ordinary, cached ones).
 hipError_t launch_hb(const void *const *send, void *const *recv, size_t count, int dtype,
-                     int nranks, const arComm *comm, int threads, uint64_t blocks, int group,
+                     int nranks, const HBConfig &cfg, int threads, uint64_t blocks, int group,
                      bool nt, hipStream_t stream);
 // `pkt_bytes` 16 selects 16-byte LL packets (the caller checks comm->ll16_ok),
 // anything else 8-byte packets; `scheme` kSchemeSequenced the sequenced flag
@@ -139,8 +168,25 @@ hipError_t launch_ll(const void *const *send, void *const *recv, size_t count, i
 // The staged form of the HB two-shot (reduce-scatter into the owner's output,
 // kernel boundary, all-gather from it), flat order only.
 hipError_t launch_hb_staged(const void *const *send, void *const *recv, size_t count, int dtype,
-                            int nranks, const arComm *comm, int threads, uint64_t blocks, bool nt,
+                            int nranks, const HBConfig &cfg, int threads, uint64_t blocks, bool nt,
                             hipStream_t stream);
+// The staged two-level form for nranks = G * group ranks in G nodes of
+// `group` (1 < group < nranks, group divides nranks): stage 1 writes each
+// node's binary32 partial to `ws` (node g at ws + g * hier_partial_stride),
+// a kernel boundary, stage 2 folds the G partials in node order, rounds once
+// and writes every output.  The caller checks that `ws` holds
+// hier_workspace_bytes(count, nranks / group) bytes, 256-byte aligned.
+hipError_t launch_hb_hier(const void *const *send, void *const *recv, size_t count, int dtype,
+                          int nranks, int group, void *ws, const HBConfig &cfg, int threads,
+                          uint64_t blocks, bool nt, hipStream_t stream);
+// Bytes between two nodes' partials, and the workspace the two-level form
+// needs: one binary32 per element per node, each node's share rounded up to
+// 256 bytes.
+inline uint64_t hier_partial_stride(uint64_t count) { return (count * 4 + 255) / 256 * 256; }
+inline uint64_t hier_workspace_bytes(uint64_t count, int nodes)
+{
+    return hier_partial_stride(count) * (uint64_t)nodes;
+}
 // Zeroes the packets and the error word and sets the sequence table to
 // arOptDebugSeqStart (0 by default).
 hipError_t launch_reset(const arComm *comm, hipStream_t stream);

@@ -134,7 +134,7 @@ hipError_t launch_stages(const StagedParams<RMAX> &p, uint32_t grid, uint32_t th
 
 template <typename T, int RMAX, bool EXACT>
 hipError_t launch_table(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, int want_threads, uint64_t want_blocks, bool nt,
+                        const HBConfig &cfg, int want_threads, uint64_t want_blocks, bool nt,
                         hipStream_t stream)
 {
     constexpr uint64_t kPerVec = 16 / T::kBytes;
@@ -151,49 +151,51 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     uint32_t threads = want_threads > 0 ? (uint32_t)want_threads : (nranks >= 32 ? 128u : 256u);
     if (threads > (uint32_t)staged_max_threads(RMAX))
         threads = (uint32_t)staged_max_threads(RMAX);
-    uint64_t grid = want_blocks > 0 ? want_blocks : (uint64_t)comm->cu_count;
+    uint64_t grid = want_blocks > 0 ? want_blocks : (uint64_t)cfg.cu_count;
     const uint64_t ntiles = (p.nvec + threads - 1) / threads;
     if (grid > ntiles)
         grid = ntiles;
     if (grid < 1)
         grid = 1;
+    if (cfg.rec != nullptr)
+        *cfg.rec = {arProtoHB, p.nvec == 0 ? 1 : 2, (uint32_t)grid, threads, 0, nt ? 1 : 0, 0, 1};
     return nt ? launch_stages<T, RMAX, EXACT, true>(p, (uint32_t)grid, threads, stream)
               : launch_stages<T, RMAX, EXACT, false>(p, (uint32_t)grid, threads, stream);
 }
 
 template <typename T>
 hipError_t launch_dtype(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, int th, uint64_t bl, bool nt, hipStream_t stream)
+                        const HBConfig &cfg, int th, uint64_t bl, bool nt, hipStream_t stream)
 {
     switch (nranks) {
-    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, comm, th, bl, nt, stream);
-    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, comm, th, bl, nt, stream);
-    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, comm, th, bl, nt, stream);
-    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, comm, th, bl, nt, stream);
-    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, comm, th, bl, nt, stream);
-    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, comm, th, bl, nt, stream);
+    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, cfg, th, bl, nt, stream);
+    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, cfg, th, bl, nt, stream);
+    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, cfg, th, bl, nt, stream);
+    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, cfg, th, bl, nt, stream);
+    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, cfg, th, bl, nt, stream);
+    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, cfg, th, bl, nt, stream);
     default: break;
     }
     if (nranks < 8)
-        return launch_table<T, 8, false>(send, recv, count, nranks, comm, th, bl, nt, stream);
+        return launch_table<T, 8, false>(send, recv, count, nranks, cfg, th, bl, nt, stream);
     if (nranks < 16)
-        return launch_table<T, 16, false>(send, recv, count, nranks, comm, th, bl, nt, stream);
-    return launch_table<T, 32, false>(send, recv, count, nranks, comm, th, bl, nt, stream);
+        return launch_table<T, 16, false>(send, recv, count, nranks, cfg, th, bl, nt, stream);
+    return launch_table<T, 32, false>(send, recv, count, nranks, cfg, th, bl, nt, stream);
 }
 
 }  // namespace
 
 hipError_t launch_hb_staged(const void *const *send, void *const *recv, size_t count, int dtype,
-                            int nranks, const arComm *comm, int threads, uint64_t blocks, bool nt,
+                            int nranks, const HBConfig &cfg, int threads, uint64_t blocks, bool nt,
                             hipStream_t stream)
 {
     switch (dtype) {
     case kBf16:
-        return launch_dtype<Bf16>(send, recv, count, nranks, comm, threads, blocks, nt, stream);
+        return launch_dtype<Bf16>(send, recv, count, nranks, cfg, threads, blocks, nt, stream);
     case kFp16:
-        return launch_dtype<Fp16>(send, recv, count, nranks, comm, threads, blocks, nt, stream);
+        return launch_dtype<Fp16>(send, recv, count, nranks, cfg, threads, blocks, nt, stream);
     default:
-        return launch_dtype<Fp32>(send, recv, count, nranks, comm, threads, blocks, nt, stream);
+        return launch_dtype<Fp32>(send, recv, count, nranks, cfg, threads, blocks, nt, stream);
     }
 }
 

@@ -240,7 +240,7 @@ hipError_t launch_unroll(const HBParams<RMAX> &p, uint32_t grid, uint32_t thread
 
 template <typename T, int RMAX, bool EXACT>
 hipError_t launch_table(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, int want_threads, uint64_t want_blocks, int group,
+                        const HBConfig &cfg, int want_threads, uint64_t want_blocks, int group,
                         bool nt, hipStream_t stream)
 {
     constexpr uint64_t kPerVec = 16 / T::kBytes;
@@ -253,10 +253,10 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     p.tail_elems = (uint32_t)(count % kPerVec);
     p.chunk_vec = p.nvec / (uint64_t)nranks;
     p.nranks = (uint32_t)nranks;
-    p.interleaved = comm->opt[arOptHBChunkLayout] == 1 ? 1u : 0u;
+    p.interleaved = cfg.interleaved ? 1u : 0u;
     p.group = group > 1 && group < nranks ? (uint32_t)group : 0u;
 
-    int u = comm->opt[arOptHBUnroll] > 0 ? (int)comm->opt[arOptHBUnroll] : 1;
+    int u = cfg.unroll > 0 ? cfg.unroll : 1;
     if (u > max_unroll(RMAX))
         u = max_unroll(RMAX);
     // Default: 256 threads (128 from 32 ranks up), one workgroup per CU --
@@ -264,7 +264,7 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     uint32_t threads = want_threads > 0 ? (uint32_t)want_threads : (nranks >= 32 ? 128u : 256u);
     if (threads > (uint32_t)hb_max_threads(RMAX))
         threads = (uint32_t)hb_max_threads(RMAX);
-    const uint64_t blocks = want_blocks > 0 ? want_blocks : (uint64_t)comm->cu_count;
+    const uint64_t blocks = want_blocks > 0 ? want_blocks : (uint64_t)cfg.cu_count;
 
     // Enough workgroups to fill the chip, but never more per chunk than the
     // largest chunk has tiles.
@@ -279,47 +279,49 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
         bpc = 1;
     p.blocks_per_chunk = (uint32_t)bpc;
     const uint32_t grid = (uint32_t)(bpc * (uint64_t)nranks);
+    if (cfg.rec != nullptr)
+        *cfg.rec = {arProtoHB, 1, grid, threads, 0, nt ? 1 : 0, (int32_t)p.group, 0};
     return launch_unroll<T, RMAX, EXACT>(p, grid, threads, u, nt, stream);
 }
 
 template <typename T>
 hipError_t launch_dtype(const void *const *send, void *const *recv, size_t count, int nranks,
-                        const arComm *comm, int th, uint64_t bl, int grp, bool nt,
+                        const HBConfig &cfg, int th, uint64_t bl, int grp, bool nt,
                         hipStream_t stream)
 {
     switch (nranks) {
-    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
-    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
-    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
-    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
-    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
-    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
+    case 1: return launch_table<T, 1, true>(send, recv, count, nranks, cfg, th, bl, grp, nt, stream);
+    case 2: return launch_table<T, 2, true>(send, recv, count, nranks, cfg, th, bl, grp, nt, stream);
+    case 4: return launch_table<T, 4, true>(send, recv, count, nranks, cfg, th, bl, grp, nt, stream);
+    case 8: return launch_table<T, 8, true>(send, recv, count, nranks, cfg, th, bl, grp, nt, stream);
+    case 16: return launch_table<T, 16, true>(send, recv, count, nranks, cfg, th, bl, grp, nt, stream);
+    case 32: return launch_table<T, 32, true>(send, recv, count, nranks, cfg, th, bl, grp, nt, stream);
     default: break;
     }
     if (nranks < 4)
-        return launch_table<T, 4, false>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
+        return launch_table<T, 4, false>(send, recv, count, nranks, cfg, th, bl, grp, nt, stream);
     if (nranks < 8)
-        return launch_table<T, 8, false>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
+        return launch_table<T, 8, false>(send, recv, count, nranks, cfg, th, bl, grp, nt, stream);
     if (nranks < 16)
-        return launch_table<T, 16, false>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
-    return launch_table<T, 32, false>(send, recv, count, nranks, comm, th, bl, grp, nt, stream);
+        return launch_table<T, 16, false>(send, recv, count, nranks, cfg, th, bl, grp, nt, stream);
+    return launch_table<T, 32, false>(send, recv, count, nranks, cfg, th, bl, grp, nt, stream);
 }
 
 }  // namespace
 
 hipError_t launch_hb(const void *const *send, void *const *recv, size_t count, int dtype,
-                     int nranks, const arComm *comm, int threads, uint64_t blocks, int group,
+                     int nranks, const HBConfig &cfg, int threads, uint64_t blocks, int group,
                      bool nt, hipStream_t stream)
 {
     switch (dtype) {
     case kBf16:
-        return launch_dtype<Bf16>(send, recv, count, nranks, comm, threads, blocks, group, nt,
+        return launch_dtype<Bf16>(send, recv, count, nranks, cfg, threads, blocks, group, nt,
                                   stream);
     case kFp16:
-        return launch_dtype<Fp16>(send, recv, count, nranks, comm, threads, blocks, group, nt,
+        return launch_dtype<Fp16>(send, recv, count, nranks, cfg, threads, blocks, group, nt,
                                   stream);
     default:
-        return launch_dtype<Fp32>(send, recv, count, nranks, comm, threads, blocks, group, nt,
+        return launch_dtype<Fp32>(send, recv, count, nranks, cfg, threads, blocks, group, nt,
                                   stream);
     }
 }

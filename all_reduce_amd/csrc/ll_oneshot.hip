@@ -482,6 +482,8 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     p.blocks_per_rank = (uint32_t)per_rank;
     const uint32_t grid = (uint32_t)(per_rank * (uint64_t)nranks);
 
+    comm->last = {arProtoLL, 1, grid, (uint32_t)threads, 8 * PW, 0,
+                  NODE == kNodeFlat ? 0 : group, 0};
     hipLaunchKernelGGL((ll_oneshot<T, RMAX, EXACT, PW, SEQ, NODE>), dim3(grid), dim3(threads), 0,
                        stream, p);
     return hipGetLastError();

@@ -27,8 +27,9 @@ __device__ inline uint32_t packet_payload(uint64_t pkt) { return (uint32_t)pkt; 
 // own flag: PW = 1 is the 8-byte packet {payload, flag}; PW = 2 the 16-byte
 // packet {payload0, flag, payload1, flag}.  A reader accepts a 16-byte
 // packet only when both flags are set, so it needs each 8-byte half to be
-// written as a unit, the same guarantee the 8-byte packet relies on.  The
-// 16-byte packet halves the memory instructions per payload byte.
+// written as a unit: the 8-byte packet has that from its 64-bit atomic store,
+// the 16-byte one only from the hardware (see below).  The 16-byte packet
+// halves the memory instructions per payload byte.
 // Indices count packets of the width from the packet region's base.
 template <int PW>
 struct PacketIO;
@@ -53,10 +54,21 @@ struct PacketIO<1> {
 // compile to on gfx950, and with the packet region as the buffer's extent, so
 // an index past the region cannot touch other memory (reads give 0, writes
 // are dropped).  The region must stay below 4 GiB (32-bit byte offsets).
+//
+// Unlike the 8-byte packet, this width rests on a property no document
+// grants: HIP offers no 128-bit atomic, and nothing in the gfx950 ISA or the
+// AMDGPU memory model says that each 8-byte half of a 128-bit store becomes
+// visible as a unit.  A half that tore could show a set flag beside a stale
+// payload.  So the 16-byte packet is an ablation that a caller must ask for
+// (arOptLLPacketBytes = 16); the defaults and the tuner use 8-byte packets,
+// whose {payload, flag} pair is one 64-bit atomic store.
 template <>
 struct PacketIO<2> {
     using V = u32x4;
     static constexpr int kCoherent = 16;             // cache-policy bit sc1
+    // Poll loads also carry the compiler's volatile bit (aux bit 31), so a
+    // re-read inside the wait loop can never be merged with an earlier one.
+    static constexpr int kPoll = kCoherent | (int)0x80000000u;
     static constexpr int kRawBufferWord3 = 0x00020000; // gfx9 raw buffer descriptor
     __amdgpu_buffer_rsrc_t rsrc;
     __device__ PacketIO(uint64_t *pkts, uint64_t region_bytes)
@@ -66,7 +78,7 @@ struct PacketIO<2> {
     }
     __device__ V load(uint64_t i) const
     {
-        return __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(uint32_t)(i * 16u), 0, kCoherent);
+        return __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(uint32_t)(i * 16u), 0, kPoll);
     }
     __device__ void store(uint64_t i, const uint32_t *w, uint32_t flag) const
     {

@@ -3,21 +3,25 @@
 
 Prints one JSON line on stdout; a markdown table goes to stderr.
 
-Default run (inputs resident in HBM before every timed region):
+Default run (inputs resident in HBM before every timed region; the built-in
+launch shapes, so that a profiled run of the same command launches the shapes
+the line reports; ``--tune`` first runs the start-up tuning of the guide's
+section 4.4, arCommTune for bf16 R = 8 up to 128 MiB per rank):
 
-* start-up tuning -- arCommTune for bf16, R = 8, every power-of-two size up to
-  128 MiB per rank (the guide's section 4.4: each size timed over launch-shape
-  candidates, the fastest kept); ``--no-tune`` uses the built-in shapes.
 * LL sweep -- R = 8 bf16, 2^k elements per rank for k = 10..19 (2 KiB to
   1 MiB), uniform[-1, 1].  As in the SGLang MSCCL++ benchmark ("SGLang 中的
   MSCCL++ All-Reduce 基准测试与推理集成指南", blog.gitcode.com, section 3.3):
   10 calls captured in one graph, ``--warmup`` untimed replays, then
   ``--steps`` replays inside one HIP event pair; latency per call = elapsed /
-  (steps * 10).  Each size also gets the guide's eager timing (2 warm-up calls,
-  then the mean of 10 back-to-back calls) for LL and HB, through prepared
-  calls (arguments marshalled once), and a timing-only plain-torch row (stack,
-  fp32 sum, cast, copy to every rank).
+  (steps * 10).  One untimed pass over every size and protocol comes first,
+  so no size is timed as the first use of anything; four more timed passes
+  per size give a median beside the guide's figure.  Each size also gets the
+  guide's eager timing (2 warm-up calls, then the mean of 10 back-to-back
+  calls) for LL and HB, through prepared calls (arguments marshalled once),
+  and a timing-only plain-torch row (stack, fp32 sum, cast, copy to every
+  rank).  Every row names the launch shape it ran (arCommGetLastLaunch).
 * LL vs HB at the decode shape 64 x 8192 with N(0, 1) values.
+* C1 -- R = 8, 1024 bf16: one out-of-place call of each protocol.
 * HB prefill -- R = 8 bf16, 8192 x 8192 elements per rank (128 MiB), N(0, 1)
   with 0.1 % of entries x1000, in place.  The roofline figure uses ``--steps``
   launches back to back inside one event pair (the kernel's average launch
@@ -25,12 +29,16 @@ Default run (inputs resident in HBM before every timed region):
   cache).  Also reported ("cold"): ``--warmup`` + ``--steps`` calls each inside
   its own event pair, with the inputs restored from a pristine copy and 512 MiB
   written to flush the last-level cache before each (untimed).
+* C5 -- R = 16 and 32, integers -4..4: 2^18 fp16 per rank (graph-replayed,
+  HB and LL) and 4096 x 7168 fp32 per rank (112 MiB, HB back to back, out of
+  place), HB with chunk = N/R beside the interleaved default layout.
 * graph_floor_us -- the per-call cost of a graph-replayed one-rank, 16-byte
   call (one workgroup), to split LL latency into launch floor and protocol;
   ll_mean_above_floor_us is the sweep's mean LL latency minus it (the floor
   differs from machine to machine, the protocol's share much less).
 * cpu_baseline -- the CPU oracle (plain C, OpenMP) timed on this host on the
-  same LL sweep inputs, a bounded sample (1.5 s of calls per size).
+  same LL sweep inputs, a bounded sample (per size the median of 3 runs of
+  0.5 s of calls on all threads, and of 0.25 s on one thread).
 * hbm_ceilings -- what the memory system delivers for the HB prefill's access
   shape without its arithmetic (tests/gpu_probe/hbm_ceiling.hip): 8 streams of
   128 MiB read only, written only (with non-temporal or ordinary stores), or
@@ -39,19 +47,21 @@ Default run (inputs resident in HBM before every timed region):
   bytes imply.
 
 ``value`` is the mean LL latency per call over the sweep in microseconds
-(lower is better).  Every timed configuration is first checked bit for bit
-against the oracle.
+(lower is better), from the guide's single timed pass per size;
+``value_median_passes`` the same from the per-size medians.  Every timed
+configuration is first checked bit for bit against the oracle.
 
 ``--configs`` adds every named workload (R = 8 small, the sweep, decode,
-prefill, and R = 16 / 32 with integer data in fp16 and fp32, tuned like the
-default run) as rows of one table, plus the hierarchical order (nodes of 8) and
-the staged HB form at their shapes: µs per call, effective GB/s (2 * R * bytes
-per rank / time), share of the 8 TB/s HBM peak, HBM GB/s from the committed
-rocprofv3 counter summaries where one covers the kernel, the oracle's time at
-1 and at all host threads and its own GB/s, parity.
+prefill, and R = 16 / 32 with integer data in fp16 and fp32) as rows of one
+table, plus the hierarchical order (nodes of 8) and the staged HB forms at
+their shapes: µs per call, effective GB/s (2 * R * bytes per rank / time),
+share of the 8 TB/s HBM peak, HBM GB/s from the committed rocprofv3 counter
+summaries where one covers the kernel, the oracle's time at 1 and at all
+host threads and its own GB/s, parity.
 
-``--only {sweep, prefill, copy, c5b}`` runs one part alone (for profiler
-passes; c5b is the fp32 R = 16 / 32 workload at 112 MiB per rank).
+``--only {sweep, prefill, copy, c5, c5b, ll_variants, ceilings}`` runs one
+part alone (for profiler passes; c5b is the fp32 R = 16 / 32 workload at
+112 MiB per rank).
 """
 from __future__ import annotations
 
@@ -65,6 +75,7 @@ import time
 METRIC = "all-reduce µs @2KiB–1MiB (R=8, hipGraph) + effective HBM GB/s vs peak"
 HBM_PEAK_GBPS = 8000.0
 CALLS_PER_GRAPH = 10
+MEDIAN_PASSES = 5
 SWEEP = list(range(10, 20))
 EAGER_WARMUP, EAGER_CALLS = 2, 10
 C5B_BYTES = 4096 * 7168 * 4  # bytes per rank of the fp32 4096 x 7168 workload
@@ -81,13 +92,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--only", choices=["all", "sweep", "prefill", "copy", "c5b", "ll_variants",
-                                       "ceilings"],
+    ap.add_argument("--only", choices=["all", "sweep", "prefill", "copy", "c5", "c5b",
+                                       "ll_variants", "ceilings"],
                     default="all", help="run one part (for profiler passes and ablations)")
     ap.add_argument("--configs", action="store_true",
                     help="also measure every named workload and print the full table")
-    ap.add_argument("--no-tune", action="store_true",
-                    help="skip the start-up tuning (arCommTune); use the built-in launch shapes")
+    ap.add_argument("--tune", action="store_true",
+                    help="run the start-up tuning (arCommTune) first, as SGLang's integration "
+                         "does; by default the built-in launch shapes are timed")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle checks")
     return ap.parse_args()
@@ -174,8 +186,9 @@ class Bench:
         return round(statistics.median(ts) * 1e3, 3)
 
     # -- timings ------------------------------------------------------------
-    def graph_us(self, sv, rv, n, proto):
-        """µs per call: 10 calls per graph, warmup replays, then steps replays."""
+    def graph_passes(self, sv, rv, n, proto, passes=1):
+        """µs per call: 10 calls per graph, warmup replays, then ``passes``
+        timed passes of steps replays, each inside its own event pair."""
         torch = self.torch
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -191,14 +204,28 @@ class Bench:
         for _ in range(self.args.warmup):
             g.replay()
         torch.cuda.synchronize()
-        t0, t1 = self.events()
-        t0.record()
-        for _ in range(self.args.steps):
-            g.replay()
-        t1.record()
-        torch.cuda.synchronize()
+        times = []
+        for _ in range(passes):
+            t0, t1 = self.events()
+            t0.record()
+            for _ in range(self.args.steps):
+                g.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1) * 1000.0 / (self.args.steps * CALLS_PER_GRAPH))
         del g
-        return t0.elapsed_time(t1) * 1000.0 / (self.args.steps * CALLS_PER_GRAPH)
+        return times
+
+    def graph_us(self, sv, rv, n, proto):
+        """µs per call of one timed pass (see graph_passes)."""
+        return self.graph_passes(sv, rv, n, proto)[0]
+
+    def launch_record(self, protocol):
+        """The launch shape of the communicator's last call, for the line."""
+        rec = self.comm.last_launch()
+        keys = ("grid", "threads", "packetBytes") if protocol == "ll" else \
+            ("grid", "threads", "nonTemporal", "kernels")
+        return {k: rec[k] for k in keys}
 
     def eager_us(self, fn):
         """2 warm-up calls, then the mean of 10 back-to-back calls.  The library
@@ -281,26 +308,32 @@ def main():
     R = 8
     result = {}
 
-    # Start-up tuning, as SGLang's MSCCL++ integration does (guide section
-    # 4.4): every power-of-two size of the bf16 R = 8 workloads, both protocols.
-    if not args.no_tune and args.only in ("all", "sweep", "prefill"):
+    # Start-up tuning (--tune), as SGLang's MSCCL++ integration does (guide
+    # section 4.4): every power-of-two size of the bf16 R = 8 workloads, both
+    # protocols.  By default the built-in shapes are timed, so that a profiled
+    # run of the same command launches exactly the shapes this line reports.
+    if args.tune and args.only in ("all", "sweep", "prefill"):
         t0 = time.perf_counter()
         B.comm.tune(torch.bfloat16, R, 128 << 20)
         result["tuning"] = {"dtype": "bf16", "nranks": R, "max_bytes_per_rank": 128 << 20,
                             "wall_s": round(time.perf_counter() - t0, 2)}
         log(f"arCommTune bf16 R=8 up to 128 MiB per rank: {result['tuning']['wall_s']} s")
 
-    # Untimed warm-up of both protocols and the graph path at the first size.
-    if args.only in ("all", "sweep"):
-        xw = inputs.make(**inputs.sweep(SWEEP[0]))
-        sv, rv = B.planes(xw)
-        for proto in ("ll", "hb"):
-            B.graph_us(sv, rv, xw.shape[1], proto)
-        del sv, rv
-
     # ---- LL sweep (HB, eager and plain torch at the same sizes) -------------
     sweep_rows = []
     if args.only in ("all", "sweep"):
+        # One untimed pass over every size and protocol first (graphs captured
+        # and replayed, eager calls), so that no size is timed as the first
+        # use of a buffer size, a graph shape or a kernel.
+        for k in SWEEP:
+            xw = inputs.make(**inputs.sweep(k))
+            sv, rv = B.planes(xw)
+            n = xw.shape[1]
+            for proto in ("ll", "hb"):
+                B.graph_passes(sv, rv, n, proto)
+                B.eager_us(B.comm.prepare(sv, rv, proto))
+            del sv, rv
+        torch.cuda.synchronize()
         for k in SWEEP:
             case = inputs.sweep(k)
             n = case["count"]
@@ -310,24 +343,21 @@ def main():
             for proto in ("ll", "hb"):
                 B.launch(sv, rv, n, proto)
                 torch.cuda.synchronize()
+                row[f"{proto}_launch"] = B.launch_record(proto)
                 row[f"{proto}_parity"] = B.parity(x, rv)
-                us = B.graph_us(sv, rv, n, proto)
-                row[f"{proto}_us"] = round(us, 3)
-                row[f"{proto}_gbps"] = gbps(R, n, 2, us)
+                # the first pass is the guide's protocol (--steps replays in one
+                # event pair); four more give the median beside it
+                times = B.graph_passes(sv, rv, n, proto, passes=MEDIAN_PASSES)
+                row[f"{proto}_us"] = round(times[0], 3)
+                row[f"{proto}_us_median"] = round(statistics.median(times), 3)
+                row[f"{proto}_gbps"] = gbps(R, n, 2, times[0])
                 row[f"{proto}_eager_us"] = round(B.eager_us(B.comm.prepare(sv, rv, proto)), 3)
             row["torch_eager_us"] = round(B.eager_us(B.torch_fn(sv, rv)), 3)
-            for proto in ("ll", "hb"):
-                shape = B.comm.tuned_shape(torch.bfloat16, R, proto, 2 * n)
-                row[f"{proto}_shape"] = (("default" if shape[0] == 0 and shape[1] == 0
-                                          else list(shape[:2])) if shape else None)
-            shape = B.comm.tuned_shape(torch.bfloat16, R, "ll", 2 * n)
-            row["ll_packet_bytes"] = shape[3] if shape else 8
-            shape = B.comm.tuned_shape(torch.bfloat16, R, "hb", 2 * n)
-            row["hb_non_temporal"] = bool(shape[4]) if shape else True
             sweep_rows.append(row)
-            log(f"sweep 2^{k}: LL {row['ll_us']:.2f} us  HB {row['hb_us']:.2f} us (graph); "
+            log(f"sweep 2^{k}: LL {row['ll_us']:.2f} (median {row['ll_us_median']:.2f}) us  "
+                f"HB {row['hb_us']:.2f} (median {row['hb_us_median']:.2f}) us (graph); "
                 f"eager LL {row['ll_eager_us']:.2f} HB {row['hb_eager_us']:.2f} "
-                f"torch {row['torch_eager_us']:.2f}")
+                f"torch {row['torch_eager_us']:.2f}; LL {row['ll_launch']}")
         if B.comm.async_error() != B.ar.arResult.arSuccess:
             raise RuntimeError("LL wait timed out during the sweep")
         result["ll_sweep"] = sweep_rows
@@ -340,8 +370,11 @@ def main():
         for proto in ("ll", "hb"):
             B.launch(sv, rv, n, proto)
             torch.cuda.synchronize()
+            dec[f"{proto}_launch"] = B.launch_record(proto)
             dec[f"{proto}_parity"] = B.parity(x, rv)
-            dec[f"{proto}_us"] = round(B.graph_us(sv, rv, n, proto), 3)
+            times = B.graph_passes(sv, rv, n, proto, passes=MEDIAN_PASSES)
+            dec[f"{proto}_us"] = round(times[0], 3)
+            dec[f"{proto}_us_median"] = round(statistics.median(times), 3)
         result["decode_64x8192"] = dec
         log(f"decode 64x8192: LL {dec['ll_us']:.2f} us  HB {dec['hb_us']:.2f} us")
         del sv, rv
@@ -358,6 +391,10 @@ def main():
         log(f"graph-replayed launch floor: {result['graph_floor_us']:.2f} us per call")
         del sv, rv
 
+    # ---- C1: R = 8, 1024 bf16, one out-of-place call -------------------------
+    if args.only in ("all", "sweep"):
+        result["c1"] = run_c1(B, inputs)
+
     # ---- HB prefill, in place, 128 MiB per rank -----------------------------
     if args.only in ("all", "prefill"):
         case = inputs.WORKLOADS["C4"]
@@ -370,7 +407,8 @@ def main():
         backup = plane.clone()
         B.launch(sv, sv, n, "hb")
         torch.cuda.synchronize()
-        pre = {"elems_per_rank": n, "bytes_per_rank": 2 * n, "in_place": True}
+        pre = {"elems_per_rank": n, "bytes_per_rank": 2 * n, "in_place": True,
+               "launch": B.launch_record("hb")}
         pre["parity"] = B.parity(x, sv)
         if args.configs:
             pre["oracle_ms_1"] = B.oracle_ms(x, 1, reps=1)
@@ -388,10 +426,6 @@ def main():
         pre["us_per_launch"] = round(avg_us, 2)
         pre["gbps"] = gbps(R, n, 2, avg_us)
         pre["gbps_cold"] = gbps(R, n, 2, mean_us)
-        shape = B.comm.tuned_shape(torch.bfloat16, R, "hb", 2 * n, in_place=True)
-        pre["shape"] = (("default" if shape[0] == 0 and shape[1] == 0 else list(shape[:2]))
-                        if shape else None)
-        pre["non_temporal"] = bool(shape[4]) if shape else True
         result["hb_prefill"] = pre
         traffic = _counter_traffic()
         result["roofline"] = {
@@ -425,28 +459,15 @@ def main():
                                       "gbps": round(2 * (1 << 30) / (us * 1e-6) / 1e9, 1)}
         del src, dst
 
-    # ---- C5b alone: fp32 R = 16 / 32 at 112 MiB per rank (for profiler passes)
-    if args.only == "c5b":
-        if not args.no_tune:
-            for R in (16, 32):
-                B.comm.tune(torch.float32, R, C5B_BYTES)
-        rows = []
-        for R in (16, 32):
-            case = inputs.integer_case(R, "fp32")
-            x = inputs.make(**case)
-            n = case["count"]
-            sv, rv = B.planes(x)
-            B.launch(sv, rv, n, "hb")
-            torch.cuda.synchronize()
-            g = torch.Generator().manual_seed(99)
-            par = B.parity(x, rv, sample=torch.randint(0, n, (1 << 20,), generator=g))
-            del x
-            us = B.back_to_back_us(sv, rv, n, "hb", args.steps)
-            rows.append({"nranks": R, "parity": par, "us_per_launch": round(us, 2),
-                         "gbps": gbps(R, n, 4, us)})
-            log(f"C5b R={R}: {us:.1f} us per launch, {gbps(R, n, 4, us):.0f} GB/s")
-            del sv, rv
-        result["c5b_hb"] = rows
+    # ---- C5: R = 16 / 32, fp16 2^18 and fp32 4096 x 7168 integers -----------
+    # (--only c5b: the fp32 part alone, for the profiler's counter passes)
+    if args.only in ("all", "c5", "c5b"):
+        if args.tune:
+            for R5 in (16, 32):
+                if args.only != "c5b":
+                    B.comm.tune(torch.float16, R5, 1 << 19)
+                B.comm.tune(torch.float32, R5, C5B_BYTES)
+        result["c5"] = run_c5(B, inputs, fp16=args.only != "c5b")
 
     # ---- HBM ceilings of the HB access pattern, beside HB itself -------------
     if args.only in ("all", "ceilings"):
@@ -506,34 +527,49 @@ def main():
     # ---- oracle on this host's cores -----------------------------------------
     if not args.no_cpu and sweep_rows:
         cores = B.threads
-        per_size = []
         t_start = time.perf_counter()
+
+        def per_call_us(xb, out, nthreads, seconds):
+            """One run: calls repeated for ``seconds`` of timed work; µs per call."""
+            reps, spent = 0, 0.0
+            while spent < seconds:
+                spent += B.orc.allreduce_into(list(xb), list(out), "bf16", nthreads=nthreads,
+                                              timed=True)
+                reps += 1
+            return spent / reps * 1e6
+
+        per_size, per_size_1 = [], []
         for k in SWEEP:
             xb = B.oracle_in(inputs.make(**inputs.sweep(k)))
             out = B.np.empty_like(xb)
-            reps, spent = 0, 0.0
-            while spent < 1.5:
-                spent += B.orc.allreduce_into(list(xb), list(out), "bf16", nthreads=cores,
-                                              timed=True)
-                reps += 1
-            per_size.append(spent / reps * 1e6)
+            per_size.append(statistics.median(per_call_us(xb, out, cores, 0.5)
+                                              for _ in range(3)))
+            per_size_1.append(statistics.median(per_call_us(xb, out, 1, 0.25)
+                                                for _ in range(3)))
         result["cpu_baseline"] = {
             "value": round(statistics.fmean(per_size), 2), "unit": "us", "cores": cores,
             "kind": "oracle",
-            "sample": (f"the oracle (plain C, OpenMP, {cores} threads) on the same LL sweep "
-                       "inputs, R=8 bf16 2^10..2^19 elements per rank, each size repeated for "
-                       "1.5 s of timed calls (15 s in all); mean µs per call over the 10 sizes"),
+            "sample": (f"the oracle (plain C, OpenMP) on the same LL sweep inputs, R=8 bf16 "
+                       f"2^10..2^19 elements per rank; per size the median of 3 runs, each "
+                       f"repeating the call for 0.5 s of timed work on {cores} threads (0.25 s "
+                       f"on 1 thread); mean µs per call over the 10 sizes"),
             "per_size_us": [round(v, 2) for v in per_size],
+            "value_1_thread": round(statistics.fmean(per_size_1), 2),
+            "per_size_us_1_thread": [round(v, 2) for v in per_size_1],
             "host_cpu": _cpu_model(),
             "wall_s": round(time.perf_counter() - t_start, 1),
         }
-        log(f"oracle on {cores} threads: mean {result['cpu_baseline']['value']:.1f} us per call")
+        log(f"oracle: mean {result['cpu_baseline']['value']:.1f} us per call on {cores} threads, "
+            f"{result['cpu_baseline']['value_1_thread']:.1f} us on 1 thread")
 
     if B.comm.async_error() != B.ar.arResult.arSuccess:
         raise RuntimeError("an LL wait timed out")
     B.comm.close()
 
     value = statistics.fmean(r["ll_us"] for r in sweep_rows) if sweep_rows else None
+    if sweep_rows:
+        result["value_median_passes"] = round(
+            statistics.fmean(r["ll_us_median"] for r in sweep_rows), 3)
     line = {
         "metric": METRIC,
         "value": round(value, 3) if value is not None else None,
@@ -555,13 +591,105 @@ def main():
             "nranks": R, "calls_per_graph": CALLS_PER_GRAPH,
             "element_type": "bf16", "accumulate": "f32 in rank order, one RNE rounding",
             "parallelism": "1 GPU, ranks simulated in HBM",
-            "tuned": not args.no_tune,
+            "tuned": args.tune,
         },
     }
     line.update(result)
     print(json.dumps(line), flush=True)
     _markdown(line)
     return 0
+
+
+def run_c1(B, inputs):
+    """C1: R = 8, 1024 bf16 uniform[-1, 1], one out-of-place call of each
+    protocol: its parity, its own time (one event pair around the single
+    eager call, launch included) and the eager mean of 10 prepared calls."""
+    torch = B.torch
+    case = inputs.WORKLOADS["C1"]
+    x = inputs.make(**case)
+    n = case["count"]
+    sv, rv = B.planes(x)
+    out = {"nranks": case["nranks"], "elems_per_rank": n, "bytes_per_rank": 2 * n}
+    for proto in ("ll", "hb"):
+        for t in rv:
+            t.view(torch.int16).fill_(-23131)  # 0xA5A5: no call result has these bits everywhere
+        torch.cuda.synchronize()
+        t0, t1 = B.events()
+        t0.record()
+        B.launch(sv, rv, n, proto)
+        t1.record()
+        torch.cuda.synchronize()
+        out[f"{proto}_single_call_us"] = round(t0.elapsed_time(t1) * 1000.0, 3)
+        out[f"{proto}_launch"] = B.launch_record(proto)
+        out[f"{proto}_parity"] = B.parity(x, rv)
+        out[f"{proto}_eager_us"] = round(B.eager_us(B.comm.prepare(sv, rv, proto)), 3)
+    log(f"C1: LL {out['ll_single_call_us']:.2f} us single call ({out['ll_eager_us']:.2f} eager "
+        f"mean), HB {out['hb_single_call_us']:.2f} ({out['hb_eager_us']:.2f}), parity "
+        f"{out['ll_parity']}/{out['hb_parity']}")
+    del sv, rv
+    return out
+
+
+def run_c5(B, inputs, fp16=True):
+    """C5: R = 16 and 32 simulated ranks with integers -4..4, HB two-shot with
+    chunk = N/R (the configured layout) beside the interleaved default:
+    C5a 2^18 fp16 per rank, graph-replayed (plus LL at the same size), and
+    C5b 4096 x 7168 fp32 per rank (112 MiB), back-to-back launches, out of
+    place.  Each row checks the oracle (C5b on 2^20 sampled columns), that
+    all R outputs are equal, and that rank 0's equals the exact integer sum."""
+    torch = B.torch
+    O = B.ar.arOption
+    rows = []
+    cases = ([("C5a", R, "fp16") for R in (16, 32)] if fp16 else []) + \
+        [("C5b", R, "fp32") for R in (16, 32)]
+    for name, R, dtype in cases:
+        case = inputs.integer_case(R, dtype)
+        n = case["count"]
+        es = 4 if dtype == "fp32" else 2
+        log(f"{name} R={R}: generating {R} x {n} {dtype} inputs")
+        x = inputs.make(**case)
+        exact = torch.zeros(n, dtype=torch.int32)
+        for r in range(R):
+            exact += x[r].to(torch.int32)
+        exact = exact.to(x.dtype).to(B.dev)
+        sv, rv = B.planes(x)
+        sample = None if name == "C5a" else torch.randint(
+            0, n, (1 << 20,), generator=torch.Generator().manual_seed(99))
+        runs = [("hb", 0, "chunk N/R"), ("hb", 1, "interleaved tiles")]
+        if name == "C5a":
+            runs.append(("ll", 1, "-"))
+        for proto, layout, lname in runs:
+            B.comm.set_option(O.arOptHBChunkLayout, layout)
+            try:
+                for t in rv:
+                    t.view(torch.int16 if es == 2 else torch.int32).fill_(-23131)
+                B.launch(sv, rv, n, proto)
+                torch.cuda.synchronize()
+                rec = B.launch_record(proto)
+                par = B.parity(x, rv, sample=sample)
+                same = all(torch.equal(rv[r], rv[0]) for r in range(1, R))
+                ex = same and torch.equal(rv[0], exact)
+                if name == "C5a":
+                    times = B.graph_passes(sv, rv, n, proto, passes=MEDIAN_PASSES)
+                    us, med, mode = times[0], statistics.median(times), "graph"
+                else:
+                    for _ in range(B.args.warmup):
+                        B.launch(sv, rv, n, proto)
+                    us = B.back_to_back_us(sv, rv, n, proto, B.args.steps)
+                    med, mode = None, "back-to-back"
+            finally:
+                B.comm.set_option(O.arOptHBChunkLayout, 1)
+            g = gbps(R, n, es, us)
+            rows.append({"config": name, "R": R, "dtype": dtype, "elems_per_rank": n,
+                         "bytes_per_rank": n * es, "proto": proto, "chunk_layout": lname,
+                         "mode": mode, "us": round(us, 3),
+                         "us_median": None if med is None else round(med, 3), "gbps": g,
+                         "pct_of_peak": round(100 * g / HBM_PEAK_GBPS, 2), "parity": par,
+                         "exact_integer_sums": ex, "launch": rec})
+            log(f"{name} R={R} {dtype} {proto} ({lname}): {us:.2f} us, {g:.0f} GB/s "
+                f"({100 * g / HBM_PEAK_GBPS:.1f}% of 8 TB/s), parity {par}, exact {ex}")
+        del x, sv, rv, exact
+    return rows
 
 
 def run_configs(B, inputs, sweep_rows, result):
@@ -626,57 +754,23 @@ def run_configs(B, inputs, sweep_rows, result):
             p["us_per_launch"], p["parity"], p.get("oracle_ms_1"), p.get("oracle_ms_T"))
         add("C4 8192x8192 in place", 8, "bf16", p["elems_per_rank"], "hb", "cold",
             p["us_mean_cold"], p["parity"], p.get("oracle_ms_1"), p.get("oracle_ms_T"))
-    # The C5 dtypes and rank counts get the start-up tuning the bench gives
-    # bf16 R = 8 (unless --no-tune): fp16 up to 512 KiB, fp32 up to 112 MiB.
-    if not B.args.no_tune:
-        t0 = time.perf_counter()
-        for R in (16, 32):
-            B.comm.tune(torch.float16, R, 1 << 19)
-            B.comm.tune(torch.float32, R, C5B_BYTES)
-        log(f"arCommTune fp16 / fp32 at R = 16, 32: {time.perf_counter() - t0:.2f} s")
-    # C5a: R = 16 / 32, 2^18 fp16 integers, both protocols, graph-timed
-    for R in (16, 32):
-        case = inputs.integer_case(R, "fp16")
-        x = inputs.make(**case)
-        n = case["count"]
-        sv, rv = B.planes(x)
-        o1, oT = B.oracle_ms(x, 1), B.oracle_ms(x, T)
-        for proto in ("ll", "hb"):
-            B.launch(sv, rv, n, proto)
-            torch.cuda.synchronize()
-            par = B.parity(x, rv)
-            exact = torch.equal(rv[0].cpu().to(torch.int64), x.to(torch.int64).sum(0))
-            add(f"C5a R={R}", R, "fp16", n, proto, "graph", B.graph_us(sv, rv, n, proto),
-                None if par is None else (par and exact), o1, oT)
-        del sv, rv
-        log(f"C5a R={R} done")
-    # C5b: R = 16 / 32, 4096 x 7168 fp32 integers, HB out of place
-    for R in (16, 32):
-        case = inputs.integer_case(R, "fp32")
-        log(f"C5b R={R}: generating {R} x {case['count']} fp32 inputs")
-        x = inputs.make(**case)
-        n = case["count"]
-        sv, rv = B.planes(x)
-        B.launch(sv, rv, n, "hb")
-        torch.cuda.synchronize()
-        g = torch.Generator().manual_seed(99)
-        sample = torch.randint(0, n, (1 << 20,), generator=g)
-        par = B.parity(x, rv, sample=sample)
-        exact = True
-        step = 1 << 22
-        for a in range(0, n, step):
-            want = x[:, a:a + step].to(torch.int32).sum(0)
-            exact &= torch.equal(rv[R - 1][a:a + step].cpu().to(torch.int32), want)
-        o1 = B.oracle_ms(x, 1, reps=1)
-        oT = B.oracle_ms(x, T, reps=1)
-        us_b2b = B.back_to_back_us(sv, rv, n, "hb", B.args.steps)
-        us_cold = statistics.fmean(B.cold_us(None, None, sv, rv, n, "hb", B.args.steps,
-                                             B.args.warmup))
-        ok = None if par is None else (par and exact)
-        add(f"C5b R={R}", R, "fp32", n, "hb", "back-to-back", us_b2b, ok, o1, oT)
-        add(f"C5b R={R}", R, "fp32", n, "hb", "cold", us_cold, ok, o1, oT)
-        del x, sv, rv
-        log(f"C5b R={R} done")
+    # C5a / C5b: the rows measured by run_c5 (both chunk layouts), with the
+    # oracle timed on the same inputs
+    oracle_times = {}
+    for row in result.get("c5", []):
+        key = (row["config"], row["R"], row["dtype"])
+        if key not in oracle_times:
+            x = inputs.make(**inputs.integer_case(row["R"], row["dtype"]))
+            reps = 3 if row["config"] == "C5a" else 1
+            oracle_times[key] = (B.oracle_ms(x, 1, reps=reps), B.oracle_ms(x, T, reps=reps))
+            del x
+        o1, oT = oracle_times[key]
+        name = f"{row['config']} R={row['R']}"
+        if row["proto"] == "hb" and row["chunk_layout"] == "chunk N/R":
+            name += " chunk N/R"
+        add(name, row["R"], row["dtype"], row["elems_per_rank"], row["proto"], row["mode"],
+            row["us"], None if row["parity"] is None else
+            (row["parity"] and row["exact_integer_sums"]), o1, oT)
 
     # NEXT-2: the hierarchical order (nodes of 8 ranks) at the C5 shapes, with
     # each protocol that can run the size
@@ -888,13 +982,26 @@ def _cpu_model() -> str:
 def _markdown(line: dict):
     rows = line.get("ll_sweep", [])
     if rows:
-        log("\n| bytes/rank | LL graph µs | HB graph µs | LL eager µs | HB eager µs | "
-            "torch eager µs | LL GB/s | HB GB/s | parity LL/HB |")
-        log("|---:|---:|---:|---:|---:|---:|---:|---:|:---:|")
+        log("\n| bytes/rank | LL graph µs (median of 5) | HB graph µs (median of 5) | LL eager µs | "
+            "HB eager µs | torch eager µs | LL GB/s | HB GB/s | LL grid x threads | "
+            "parity LL/HB |")
+        log("|---:|---:|---:|---:|---:|---:|---:|---:|---|:---:|")
         for r in rows:
-            log(f"| {r['bytes_per_rank']} | {r['ll_us']:.2f} | {r['hb_us']:.2f} | "
+            ll = r["ll_launch"]
+            log(f"| {r['bytes_per_rank']} | {r['ll_us']:.2f} ({r['ll_us_median']:.2f}) | "
+                f"{r['hb_us']:.2f} ({r['hb_us_median']:.2f}) | "
                 f"{r['ll_eager_us']:.2f} | {r['hb_eager_us']:.2f} | {r['torch_eager_us']:.2f} | "
-                f"{r['ll_gbps']:.0f} | {r['hb_gbps']:.0f} | {r['ll_parity']}/{r['hb_parity']} |")
+                f"{r['ll_gbps']:.0f} | {r['hb_gbps']:.0f} | {ll['grid']} x {ll['threads']} | "
+                f"{r['ll_parity']}/{r['hb_parity']} |")
+    c5 = line.get("c5", [])
+    if c5:
+        log("\n| config | R | dtype | proto | chunk layout | mode | µs | GB/s | % of 8 TB/s | "
+            "parity | exact sums |")
+        log("|---|---:|---|---|---|---|---:|---:|---:|:---:|:---:|")
+        for r in c5:
+            log(f"| {r['config']} | {r['R']} | {r['dtype']} | {r['proto']} | {r['chunk_layout']} | "
+                f"{r['mode']} | {r['us']:.2f} | {r['gbps']:.0f} | {r['pct_of_peak']:.1f} | "
+                f"{r['parity']} | {r['exact_integer_sums']} |")
 
 
 if __name__ == "__main__":

@@ -13,8 +13,9 @@
  * ncclAllReduce), with the R rank pointers of the simulated group passed as
  * arrays.  Two protocols from the page's MemoryChannel table are offered:
  *
- *   arProtoLL  low latency: one kernel, flag-carrying 8-byte (or 16-byte)
- *              packets, polled per wavefront; meant for decode-size messages.
+ *   arProtoLL  low latency: one kernel, flag-carrying 8-byte packets (16-byte
+ *              ones as an option), polled per wavefront; meant for
+ *              decode-size messages.
  *   arProtoHB  high bandwidth: two-shot reduce-scatter by chunk then
  *              all-gather, 128-bit bulk loads and stores, no flags; meant for
  *              prefill-size messages.  A staged form with a kernel boundary
@@ -123,18 +124,22 @@ typedef enum {
      * nodes second ("SGLang 中的 MSCCL++ All-Reduce 基准测试与推理集成指南",
      * section 4.4: multi-node algorithms for TP = 16 / 32).  0 (default), 1
      * or >= nranks: the flat order 0..R-1.  A value in between must divide
-     * nranks (else arInvalidUsage).  The two ablations keep the flat order:
-     * with arOptHBStaged, HB returns arUnsupported, and with the sequenced LL
-     * flag scheme, LL does (arProtoAuto then runs HB). */
+     * nranks (else arInvalidUsage).  The fused HB kernel and the LL kernel
+     * fold the order in registers; with arOptHBStaged the HB call runs the
+     * staged two-level form (see there).  The sequenced LL flag scheme keeps
+     * the flat order: with it, LL returns arUnsupported (arProtoAuto then
+     * runs HB). */
     arOptNodeRanks = 9,
-    /* LL: packet width in bytes.  8: a 4-byte payload next to a 4-byte flag;
-     * 16: two such pairs, written and read as one 16-byte access (half the
-     * memory instructions per payload byte).  0 (default): the width the
-     * tuner chose for the message size, else the built-in default's for the
-     * rank count and size (16 bytes from 256 KiB per rank up to 8 ranks and
-     * from 128 KiB above 16 ranks; 8 bytes otherwise).  16 needs the communicator's
-     * packet memory below 4 GiB (maxRanks * maxLLBytesPerRank * 2), else
-     * setting it returns arUnsupported. */
+    /* LL: packet width in bytes.  8: a 4-byte payload next to a 4-byte flag,
+     * written as one 64-bit atomic store, so a reader that sees the flag also
+     * sees the payload.  16: two such pairs, written and read as one 16-byte
+     * access (half the memory instructions per payload byte); an ablation,
+     * because it needs each 8-byte half of a 128-bit store to become visible
+     * as a unit, which neither HIP (no 128-bit atomics) nor any gfx950
+     * document guarantees.  0 (default) and 8: 8-byte packets; the tuner
+     * times 8-byte packets only.  16 needs the communicator's packet memory
+     * below 4 GiB (maxRanks * maxLLBytesPerRank * 2), else setting it returns
+     * arUnsupported. */
     arOptLLPacketBytes = 10,
     /* HB: 1 = the staged two-shot, an ablation of the fused default: the
      * reduce-scatter writes each reduced chunk to its owner rank's output
@@ -143,8 +148,20 @@ typedef enum {
      * 一样可编程", "MemoryChannel"), and the all-gather copies each chunk from
      * its owner to the other outputs.  Same result bits; 2 * bytes per rank
      * more traffic and one more launch.  Launch shape from arOptHBThreads /
-     * arOptHBBlocks or the defaults, never the tuned table.  With
-     * arOptNodeRanks set, HB calls return arUnsupported.  0 (default): fused. */
+     * arOptHBBlocks or the defaults, never the tuned table.  0 (default): fused.
+     *
+     * With arOptNodeRanks = L set as well (R = G * L ranks in G nodes), the
+     * staged two-level form of the same guide's section 4.4 multi-node
+     * algorithms, and of the high-throughput mode of "NCCL EP统一MoE通信生态：
+     * 打破碎片化，加速大模型推理新纪元" (itsolotime.com/archives/27456,
+     * section 3.2: inside the node first, between nodes second): stage 1 is a
+     * node-local reduce-scatter that writes each node's binary32 partial to
+     * the communicator's workspace (arCommSetWorkspace: at least
+     * G * roundup(count * 4, 256) bytes, else arInvalidUsage), a kernel
+     * boundary separates the levels, and stage 2 folds the G partials of each
+     * position in node order, rounds once and all-gathers the result to every
+     * rank.  Same bits as the fused kernel in that order; 2 * G * count * 4
+     * bytes more traffic. */
     arOptHBStaged = 11,
     /* LL: how a packet left by an earlier call is kept from looking ready.
      * 0 (default): the reader zeroes every packet it has consumed, so packet
@@ -171,7 +188,16 @@ typedef enum {
     arOptTuneFreshInputs = 14
 } arOption_t;
 
-/* Create a communicator on `device` for groups of up to `maxRanks` (1..32)
+/* The communicator is the long-lived group resource of an NCCL-style
+ * collective library: it owns the buffers that every call reuses, so set-up
+ * is paid once and each call only enqueues work (the group/handle split of
+ * "NCCL EP统一MoE通信生态：打破碎片化，加速大模型推理新纪元",
+ * itsolotime.com/archives/27456, section 2.3, 资源生命周期管理).  Its LL
+ * packet memory must exist before a graph capture starts, because nothing can
+ * be allocated inside one ("SGLang 中的 MSCCL++ All-Reduce 基准测试与推理集成指南",
+ * blog.gitcode.com, section 1: the all-reduce runs under CUDA Graph decode).
+ *
+ * Create a communicator on `device` for groups of up to `maxRanks` (1..32)
  * simulated ranks and LL messages of up to `maxLLBytesPerRank` bytes per rank.
  * It owns device memory for the LL packets (2 * maxRanks * maxLLBytesPerRank
  * bytes, each rank's share rounded up to 512 bytes: packets are half payload,
@@ -184,23 +210,54 @@ typedef enum {
  * arHipError if the device or memory is not available. */
 arResult_t arCommCreate(arComm_t *comm, int device, int maxRanks, size_t maxLLBytesPerRank);
 
-/* Free the communicator.  Work that uses it must have finished. */
+/* Free the communicator and its device memory: the end of the long-lived
+ * group resource (NCCL EP article, itsolotime.com/archives/27456, section
+ * 2.3).  Work that uses it must have finished. */
 arResult_t arCommDestroy(arComm_t comm);
 
-/* Enqueue, on `stream`, a kernel that clears the LL packets, the sequence
+/* Recovery of the group resource after a failed call, so the communicator
+ * can be reused instead of rebuilt (NCCL EP article, section 2.3: the group's
+ * buffers are long-lived and reused across calls).
+ * Enqueue, on `stream`, a kernel that clears the LL packets, the sequence
  * table (to arOptDebugSeqStart, 0 by default) and the asynchronous error, so
  * that the communicator can be used again after a timeout (an LL call that
  * timed out may leave packets set; LL results are undefined until the reset).
  * No allocation and no memset node: safe to capture in a graph. */
 arResult_t arCommReset(arComm_t comm, arStream_t stream);
 
-/* Read the asynchronous error recorded by earlier kernels: arSuccess or
+/* Error reporting without aborts: the pages' integration never aborts on a
+ * failed guard but reports it and falls back ("SGLang 中的 MSCCL++ All-Reduce
+ * 基准测试与推理集成指南", sections 4.3 and 5); a device-side failure (an LL
+ * wait that ran out) is kept in the communicator and read here.
+ * Read the asynchronous error recorded by earlier kernels: arSuccess or
  * arTimeout.  Synchronises the device first.  The error stays set until
  * arCommReset. */
 arResult_t arCommGetAsyncError(arComm_t comm, arResult_t *asyncError);
 
-/* Set or read one option (arOption_t) of the communicator.  Values outside an
- * option's range give arInvalidArgument. */
+/* Device memory for the communicator's staged two-level HB form (arOptHBStaged
+ * with arOptNodeRanks): the node partials that the node-local reduce-scatter
+ * writes and the cross-node fold reads -- the scratch buffers that a
+ * multi-node MSCCL++ algorithm exchanges between its levels ("SGLang 中的
+ * MSCCL++ All-Reduce 基准测试与推理集成指南", section 4.4).  The caller owns
+ * it: the library never allocates it, so it can come from the caller's
+ * allocator and be set before a graph capture.  It must stay valid, and not
+ * be used for anything else, while calls that use it are pending or captured.
+ * `workspace` 256-byte aligned device memory of `bytes` bytes on the
+ * communicator's device; NULL with 0 detaches it.  No HIP call.
+ * Returns arInvalidArgument for a NULL comm, a pointer without a size (or the
+ * reverse), or a misaligned pointer.  A call that needs more than `bytes`
+ * returns arInvalidUsage, and one whose rank buffers overlap the part it
+ * needs arInvalidArgument. */
+arResult_t arCommSetWorkspace(arComm_t comm, void *workspace, size_t bytes);
+
+/* Set or read one option (arOption_t) of the communicator: the per-size
+ * launch parameters (workgroups, threads per workgroup) that SGLang's MSCCL++
+ * integration times and keeps ("SGLang 中的 MSCCL++ All-Reduce 基准测试与推理
+ * 集成指南", section 4.4), the protocol details of the MemoryChannel table's
+ * LL and HB protocols ("MSCCL++：让 GPU 通信像 CUDA 一样可编程",
+ * infinitensor.com/news/50, "MemoryChannel"), the two-level order of that
+ * guide's section 4.4 multi-node algorithms, and test hooks.  Values outside
+ * an option's range give arInvalidArgument. */
 arResult_t arCommSetOption(arComm_t comm, arOption_t option, int64_t value);
 arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
 
@@ -221,9 +278,9 @@ arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
  * power of two) and mode (in place: recvbufs[r] == sendbufs[r] for every
  * rank) unless arOptLLThreads/arOptLLBlocksPerRank (LL) or arOptHBThreads/
  * arOptHBBlocks (HB), arOptLLPacketBytes or arOptLLFlagScheme are set;
- * arProtoAuto then picks the faster protocol.  LL candidates cover both
- * packet widths, in the default flag scheme; HB candidates both access
- * policies unless arOptHBNonTemporal fixes one.
+ * arProtoAuto then picks the faster protocol.  LL candidates use 8-byte
+ * packets in the default flag scheme; HB candidates both access policies
+ * unless arOptHBNonTemporal fixes one.
  * Tuning again overwrites the table; sizes never tuned use built-in defaults.
  *
  * Each candidate is timed the way latency-sensitive callers run the library:
@@ -241,23 +298,48 @@ arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
 arResult_t arCommTune(arComm_t comm, arDataType_t dtype, int nranks, size_t maxBytesPerRank,
                       arStream_t stream);
 
-/* One entry of the tuned table. */
+/* One entry of the tuned table (the guide's best_configs entry for one size,
+ * section 4.4). */
 typedef struct {
     int tuned;        /* 0: this size was never tuned (the rest is 0) */
     int threads;      /* threads per workgroup that won; 0 with blocks 0: the default shape */
     int blocks;       /* workgroups that won (HB: the grid; LL: per rank) */
-    int packetBytes;  /* LL: the packet width that won, 8 or 16; HB: 0 */
+    int packetBytes;  /* LL: the packet width it was timed with (8); HB: 0 */
     int nonTemporal;  /* HB: 1 if non-temporal accesses won, 0 if cached ones; LL: 0 */
     float us;         /* time per call measured for it, in microseconds */
 } arTunedShape_t;
 
-/* The tuned entry for (dtype, nranks, protocol LL or HB) at a message of
+/* Look-up of the tuned table as the guide's section 4.4 describes it: the
+ * message size rounded up to a power of two selects the entry.
+ * The tuned entry for (dtype, nranks, protocol LL or HB) at a message of
  * bytesPerRank bytes, in place (inPlace = 1) or out of place (inPlace = 0),
  * copied to *shape.  Returns arInvalidArgument for NULL pointers or
  * out-of-range arguments. */
 arResult_t arCommGetTunedShape(arComm_t comm, arDataType_t dtype, int nranks,
                                arProtocol_t protocol, size_t bytesPerRank, int inPlace,
                                arTunedShape_t *shape);
+
+/* The launch behind the communicator's most recent call (arAllReduce, or a
+ * tuning candidate of arCommTune): the (workgroups, threads per workgroup)
+ * pair that SGLang's tuner picks per size ("SGLang 中的 MSCCL++ All-Reduce
+ * 基准测试与推理集成指南", section 4.4), with the protocol details that go
+ * with it, so that a caller or a profile can name the shape a timed call ran.
+ * protocol is -1 before the first launch; a call that enqueued nothing
+ * (count 0, or an error) leaves the record as it was. */
+typedef struct {
+    int protocol;      /* arProtoLL or arProtoHB (arProtoAuto resolved); -1: none yet */
+    int kernels;       /* kernels the call enqueued (2 for a staged HB form) */
+    unsigned grid;     /* workgroups of its (first) kernel */
+    unsigned threads;  /* threads per workgroup */
+    int packetBytes;   /* LL: packet width, 8 or 16; HB: 0 */
+    int nonTemporal;   /* HB: 1 non-temporal accesses, 0 cached; LL: 0 */
+    int nodeRanks;     /* ranks per node of a hierarchical order; 0: flat */
+    int staged;        /* HB: 1 for a staged form; else 0 */
+} arLaunchInfo_t;
+
+/* Copy the record of the most recent launch to *info.  Returns
+ * arInvalidArgument for NULL pointers. */
+arResult_t arCommGetLastLaunch(arComm_t comm, arLaunchInfo_t *info);
 
 /* The sum all-reduce.
  *
@@ -294,10 +376,13 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
                        arDataType_t dtype, arRedOp_t op, int nranks, arProtocol_t protocol,
                        arComm_t comm, arStream_t stream);
 
-/* Static description of a result code. */
+/* Static description of a result code (arUnsupported is the guide's
+ * "fall back to another all-reduce", sections 4.3 and 5). */
 const char *arGetErrorString(arResult_t result);
 
-/* AR_VERSION of the built library. */
+/* AR_VERSION of the built library, so a caller can check the ABI it loaded
+ * (the NCCL-compatible API of "MSCCL++：让 GPU 通信像 CUDA 一样可编程",
+ * "第一层：Collective API", is a drop-in replacement and needs one). */
 int arGetVersion(void);
 
 #ifdef __cplusplus

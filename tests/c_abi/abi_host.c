@@ -29,6 +29,13 @@ int main(int argc, char **argv)
                offsetof(arTunedShape_t, threads), offsetof(arTunedShape_t, blocks),
                offsetof(arTunedShape_t, packetBytes), offsetof(arTunedShape_t, nonTemporal),
                offsetof(arTunedShape_t, us));
+        printf("arLaunchInfo_t %zu protocol %zu kernels %zu grid %zu threads %zu "
+               "packetBytes %zu nonTemporal %zu nodeRanks %zu staged %zu\n",
+               sizeof(arLaunchInfo_t), offsetof(arLaunchInfo_t, protocol),
+               offsetof(arLaunchInfo_t, kernels), offsetof(arLaunchInfo_t, grid),
+               offsetof(arLaunchInfo_t, threads), offsetof(arLaunchInfo_t, packetBytes),
+               offsetof(arLaunchInfo_t, nonTemporal), offsetof(arLaunchInfo_t, nodeRanks),
+               offsetof(arLaunchInfo_t, staged));
         printf("arResult_t %zu arDataType_t %zu arRedOp_t %zu arProtocol_t %zu arOption_t %zu\n",
                sizeof(arResult_t), sizeof(arDataType_t), sizeof(arRedOp_t),
                sizeof(arProtocol_t), sizeof(arOption_t));
@@ -56,6 +63,9 @@ int main(int argc, char **argv)
     arTunedShape_t shape;
     expect(arCommGetTunedShape(NULL, arBfloat16, 8, arProtoHB, 4096, 0, &shape) ==
                arInvalidArgument, "tuned shape of a NULL communicator");
+    arLaunchInfo_t info;
+    expect(arCommGetLastLaunch(NULL, &info) == arInvalidArgument,
+           "last launch of a NULL communicator");
     if (failures == 0)
         printf("ok\n");
     return failures == 0 ? 0 : 1;

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     lib = ar.library()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
@@ -167,20 +167,20 @@ def test_plain_c_caller_host_side():
 
 
 def test_binding_mirrors_the_c_layout():
-    """The ctypes mirror of arTunedShape_t has the C struct's size and field
-    offsets, and the enums are int-sized as the binding assumes."""
+    """The ctypes mirrors of arTunedShape_t and arLaunchInfo_t have the C
+    structs' sizes and field offsets, and the enums are int-sized as the binding assumes."""
     from c_abi import build as cbuild
     exe = cbuild.HERE / "abi_host.bin"
     if not exe.exists() or exe.stat().st_mtime < ar.LIBRARY.stat().st_mtime:
         cbuild.build()
     res = subprocess.run([str(exe), "layout"], capture_output=True, text=True, timeout=60)
     assert res.returncode == 0, res.stdout + res.stderr
-    shape_line, enum_line = res.stdout.strip().splitlines()
-    words = shape_line.split()
-    c_layout = {words[i]: int(words[i + 1]) for i in range(0, len(words), 2)}
-    m = ar.arTunedShape
-    py_layout = {"arTunedShape_t": ctypes.sizeof(m)}
-    py_layout.update({name: getattr(m, name).offset for name, _ in m._fields_})
-    assert py_layout == c_layout
+    shape_line, info_line, enum_line = res.stdout.strip().splitlines()
+    for line, m in ((shape_line, ar.arTunedShape), (info_line, ar.arLaunchInfo)):
+        words = line.split()
+        c_layout = {words[i]: int(words[i + 1]) for i in range(0, len(words), 2)}
+        py_layout = {words[0]: ctypes.sizeof(m)}
+        py_layout.update({name: getattr(m, name).offset for name, _ in m._fields_})
+        assert py_layout == c_layout
     words = enum_line.split()
     assert all(int(words[i + 1]) == ctypes.sizeof(ctypes.c_int) for i in range(0, len(words), 2))

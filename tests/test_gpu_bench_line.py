@@ -42,7 +42,7 @@ def _contract(line, steps, warmup):
 
 
 def test_sweep_line():
-    line = _run("--only", "sweep", "--steps", "2", "--warmup", "1", "--no-cpu", "--no-tune")
+    line = _run("--only", "sweep", "--steps", "2", "--warmup", "1", "--no-cpu")
     _contract(line, 2, 1)
     rows = line["ll_sweep"]
     assert [r["bytes_per_rank"] for r in rows] == [2 << k for k in range(10, 20)]
@@ -54,10 +54,21 @@ def test_sweep_line():
         line["value"] - line["graph_floor_us"], abs=2e-3)
     assert line["ms_per_step"] == pytest.approx(sum(r["ll_us"] for r in rows) * 10 / 1000,
                                                 abs=1e-3)
+    # every row names the launch it timed: LL with 8-byte packets at the
+    # built-in shape, HB with one kernel
+    for r in rows:
+        assert r["ll_launch"]["packetBytes"] == 8 and r["ll_launch"]["grid"] % 8 == 0
+        assert r["hb_launch"]["kernels"] == 1 and r["hb_launch"]["grid"] % 8 == 0
+        assert r["ll_us_median"] > 0 and r["hb_us_median"] > 0
+    assert line["value_median_passes"] == pytest.approx(
+        sum(r["ll_us_median"] for r in rows) / len(rows), abs=2e-3)
+    assert line["config"]["tuned"] is False
+    c1 = line["c1"]
+    assert c1["ll_parity"] and c1["hb_parity"] and c1["elems_per_rank"] == 1024
 
 
 def test_prefill_roofline():
-    line = _run("--only", "prefill", "--steps", "3", "--warmup", "1", "--no-cpu", "--no-tune")
+    line = _run("--only", "prefill", "--steps", "3", "--warmup", "1", "--no-cpu")
     _contract(line, 3, 1)
     assert line["hb_prefill"]["parity"] is True
     roof = line["roofline"]
@@ -68,3 +79,19 @@ def test_prefill_roofline():
     assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], abs=1e-4)
     # traffic is the committed counter reading (checked against the sources on the CPU)
     assert roof["traffic"] is None or abs(roof["traffic"] / (2 << 30) - 1) < 0.01
+
+
+def test_c5_rows():
+    """C5 at R = 16 and 32: both HB chunk layouts (chunk = N/R as configured,
+    and interleaved tiles), LL at the fp16 size; every row bit-exact against
+    the oracle and equal to the exact integer sums."""
+    line = _run("--only", "c5", "--steps", "2", "--warmup", "1", "--no-cpu")
+    _contract(line, 2, 1)
+    rows = line["c5"]
+    assert len(rows) == 2 * 3 + 2 * 2
+    assert all(r["parity"] and r["exact_integer_sums"] for r in rows)
+    assert {r["chunk_layout"] for r in rows if r["proto"] == "hb"} == {"chunk N/R",
+                                                                          "interleaved tiles"}
+    for r in rows:
+        assert r["gbps"] == pytest.approx(
+            2 * r["R"] * r["bytes_per_rank"] / (r["us"] * 1e-6) / 1e9, rel=2e-3)

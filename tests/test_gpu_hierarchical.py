@@ -151,16 +151,22 @@ def test_grouping_rules(comm):
     with grouped(comm, 8):  # both protocols and auto run the hierarchical order
         for proto in (0, 1, 2):
             assert ar.arAllReduce(q, q, 64, 0, 0, 16, proto, comm.handle, s) == ar.arResult.arSuccess
-    # the two ablations keep the flat order
-    for opt, value, proto in ((ar.arOption.arOptLLFlagScheme, 1, 0),
-                              (ar.arOption.arOptHBStaged, 1, 1)):
-        comm.set_option(opt, value)
-        try:
-            with grouped(comm, 8):
-                assert ar.arAllReduce(q, q, 64, 0, 0, 16, proto, comm.handle, s) == \
-                    ar.arResult.arUnsupported
-        finally:
-            comm.set_option(opt, 0)
+    # the sequenced LL ablation keeps the flat order
+    comm.set_option(ar.arOption.arOptLLFlagScheme, 1)
+    try:
+        with grouped(comm, 8):
+            assert ar.arAllReduce(q, q, 64, 0, 0, 16, 0, comm.handle, s) == \
+                ar.arResult.arUnsupported
+    finally:
+        comm.set_option(ar.arOption.arOptLLFlagScheme, 0)
+    # the staged HB form becomes the two-level form, which needs a workspace
+    comm.set_option(ar.arOption.arOptHBStaged, 1)
+    try:
+        with grouped(comm, 8):
+            assert ar.arAllReduce(q, q, 64, 0, 0, 16, 1, comm.handle, s) == \
+                ar.arResult.arInvalidUsage
+    finally:
+        comm.set_option(ar.arOption.arOptHBStaged, 0)
     comm.set_option(ar.arOption.arOptLLFlagScheme, 1)
     try:
         with grouped(comm, 8):  # auto avoids the sequenced LL scheme under a hierarchy

@@ -4,6 +4,8 @@ The bar is bit-exact equality (NaNs by class): the kernels sum in the same
 rank order 0..R-1 in binary32 and round once with RNE, like the oracle.
 Inputs come from ``all_reduce_amd.inputs`` (seeded), never from the GPU path.
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -64,28 +66,57 @@ def test_c4_prefill_in_place_full_size(comm, orc):
     assert int((rev[0] != want[0]).sum()) > 0
 
 
-@pytest.mark.parametrize("R", [16, 32])
-def test_c5_fp16_integer_sums(comm, orc, R):
-    case = inputs.integer_case(R, "fp16")
-    x = inputs.make(**case)
-    got = check(comm, orc, x, "hb")
-    exact = x.to(torch.int64).sum(0)
-    assert torch.equal(got[0].to(torch.int64), exact)
-
-
-@pytest.mark.parametrize("R", [16, 32])
-def test_c5_fp32_integer_sums_full_size(comm, orc, R):
-    """R x 4096*7168 fp32: exact integer sums everywhere, oracle on a sample."""
-    case = inputs.integer_case(R, "fp32")
-    x = inputs.make(**case)
-    got = run_allreduce(comm, x, "hb")
-    exact = x.to(torch.int64).sum(0)
+@functools.lru_cache(maxsize=2)
+def _c5_case(R, dtype):
+    """C5 inputs (integers -4..4) and their exact sums, computed once per shape."""
+    x = inputs.make(**inputs.integer_case(R, dtype))
+    exact = torch.zeros(x.shape[1], dtype=torch.int32)
     for r in range(R):
-        assert torch.equal(got[r].to(torch.int64), exact), f"rank {r}"
+        exact += x[r].to(torch.int32)
+    return x, exact
+
+
+@pytest.fixture
+def chunk_layout(comm, request):
+    """HB chunk layout for one test (0: contiguous N/R chunks, 1: interleaved
+    tiles), restored to the default afterwards."""
+    comm.set_option(ar.arOption.arOptHBChunkLayout, request.param)
+    yield request.param
+    comm.set_option(ar.arOption.arOptHBChunkLayout, 1)
+
+
+@pytest.mark.parametrize("inplace", [False, True], ids=["out", "inplace"])
+@pytest.mark.parametrize("chunk_layout", [0, 1], ids=["chunk_N_over_R", "interleaved"],
+                         indirect=True)
+@pytest.mark.parametrize("R", [16, 32])
+def test_c5_fp16_integer_sums(comm, orc, R, chunk_layout, inplace):
+    """R x 2^18 fp16 integers, HB with chunk = N/R (the configured layout) and
+    with interleaved tiles: oracle on every element, exact integer sums."""
+    x, exact = _c5_case(R, "fp16")
+    got = check(comm, orc, x, "hb", inplace=inplace,
+                what=f"C5 fp16 R={R} layout={chunk_layout} inplace={inplace}")
+    for r in range(R):
+        assert torch.equal(got[r].to(torch.int32), exact), f"rank {r}"
+
+
+@pytest.mark.parametrize("inplace", [False, True], ids=["out", "inplace"])
+@pytest.mark.parametrize("chunk_layout", [0, 1], ids=["chunk_N_over_R", "interleaved"],
+                         indirect=True)
+@pytest.mark.parametrize("R", [16, 32])
+def test_c5_fp32_integer_sums_full_size(comm, orc, R, chunk_layout, inplace):
+    """R x 4096*7168 fp32, HB with chunk = N/R (the configured layout) and with
+    interleaved tiles: exact integer sums on every element of every rank, the
+    oracle on 2^20 sampled columns."""
+    x, exact = _c5_case(R, "fp32")
+    got = run_allreduce(comm, x, "hb", inplace=inplace)
+    exact_f = exact.to(torch.float32)
+    for r in range(R):
+        assert torch.equal(got[r], exact_f), f"rank {r}"
     g = torch.Generator().manual_seed(99)
     idx = torch.randint(0, x.shape[1], (1 << 20,), generator=g)
     want = expect(orc, x[:, idx].contiguous())
-    assert_parity(got[:, idx].contiguous(), want, f"C5 fp32 R={R} sampled")
+    assert_parity(got[:, idx].contiguous(), want,
+                  f"C5 fp32 R={R} layout={chunk_layout} inplace={inplace} sampled")
 
 
 # ---- the prepared call ---------------------------------------------------------
@@ -128,15 +159,83 @@ def test_prepared_call_reports_errors(comm):
         comm.prepare(sv, sv[:1], "hb")
 
 
+def test_prepared_call_after_close_raises(orc):
+    """A prepared call reads the communicator's handle at each call: after the
+    communicator is closed it raises instead of passing a freed handle on."""
+    R, N = 4, 1000
+    x = inputs.make(R, N, "fp16", "normal", seed=53)
+    c = ar.Comm(device="cuda:0", max_ranks=R, max_ll_bytes_per_rank=1 << 12)
+    _, sv = ar.rank_buffers(R, N, torch.float16, c.device)
+    for r in range(R):
+        sv[r].copy_(x[r])
+    call = c.prepare(sv, None, "ll")
+    note("prepared LL before close")
+    call()
+    torch.cuda.synchronize()
+    assert_parity(torch.stack([t.cpu() for t in sv]), expect(orc, x), "prepared before close")
+    c.close()
+    with pytest.raises(ValueError):
+        call()
+
+
+def test_comm_on_cuda_without_index(orc):
+    """Comm(device="cuda") is the current device: tensors on "cuda:0" match it."""
+    torch.cuda.set_device(0)
+    with ar.Comm(device="cuda", max_ranks=2, max_ll_bytes_per_rank=1 << 12) as c:
+        assert c.device == torch.device("cuda", 0)
+        x = inputs.make(2, 300, "bf16", "normal", seed=54)
+        _, sv = ar.rank_buffers(2, 300, torch.bfloat16, "cuda:0")
+        for r in range(2):
+            sv[r].copy_(x[r])
+        note("Comm(device='cuda') all_reduce")
+        c.all_reduce(sv, protocol="hb")
+        torch.cuda.synchronize()
+        assert_parity(torch.stack([t.cpu() for t in sv]), expect(orc, x), "cuda without index")
+
+
+def test_last_launch_record(orc):
+    """arCommGetLastLaunch names the shape each call launched: the built-in
+    LL shape (8-byte packets), the HB default (one workgroup per CU,
+    non-temporal), the staged HB form (two kernels), a 16-byte-packet LL call
+    only when asked for, and no change for a call that enqueues nothing."""
+    with ar.Comm(device="cuda:0", max_ranks=8, max_ll_bytes_per_rank=1 << 20) as c:
+        assert c.last_launch() is None
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        x = inputs.make(8, 1 << 10, "bf16", "uniform", seed=55)
+        run_allreduce(c, x, "ll")
+        rec = c.last_launch()
+        assert rec["protocol"] == ar.arProtocol.arProtoLL and rec["packetBytes"] == 8
+        assert (rec["grid"], rec["threads"], rec["kernels"]) == (8, 256, 1)
+        y = inputs.make(8, 1 << 19, "bf16", "uniform", seed=56)
+        run_allreduce(c, y, "hb")
+        rec = c.last_launch()
+        assert rec["protocol"] == ar.arProtocol.arProtoHB and rec["nonTemporal"] == 1
+        # one workgroup per CU, rounded up to whole chunks, at most the 32
+        # tiles of 256 vectors that each of the 8 interleaved chunks has
+        assert (rec["grid"], rec["threads"], rec["staged"]) == (min(-(-cus // 8), 32) * 8, 256, 0)
+        c.set_option(ar.arOption.arOptHBStaged, 1)
+        run_allreduce(c, y, "hb")
+        assert c.last_launch()["kernels"] == 2 and c.last_launch()["staged"] == 1
+        c.set_option(ar.arOption.arOptHBStaged, 0)
+        c.set_option(ar.arOption.arOptLLPacketBytes, 16)
+        run_allreduce(c, x, "ll")
+        assert c.last_launch()["packetBytes"] == 16
+        before = c.last_launch()
+        rc = ar.arAllReduce([0] * 8, [0] * 8, 0, ar.arDataType.arBfloat16, ar.arRedOp.arSum, 8,
+                            ar.arProtocol.arProtoLL, c.handle,
+                            torch.cuda.current_stream().cuda_stream)
+        assert rc == ar.arResult.arSuccess and c.last_launch() == before
+
+
 # ---- shapes, tails and rank counts --------------------------------------------
 @pytest.mark.parametrize("R", [3, 8, 12, 16, 24, 32])
 @pytest.mark.parametrize("kib", [2, 8, 64, 128, 256, 512, 1024])
 def test_ll_default_shape_table(comm, orc, R, kib):
     """LL at its built-in default launch shape (no tuning, no shape options) in
     each rank class of the default table (up to 8, 9-16, 17-32 ranks) and at
-    sizes spanning its columns, including the 16-byte-packet and
-    128-workgroup-per-rank entries; one element short of each power of two,
-    so every size ends in a partial packet or vector."""
+    sizes spanning its columns, including the 128-workgroup-per-rank
+    entries; one element short of each power of two, so every size ends in a
+    partial packet or vector."""
     N = kib * 512 - 1
     x = inputs.make(R, N, "bf16", "normal", seed=3000 + R * 7 + kib)
     check(comm, orc, x, "ll", what=f"ll default shape R={R} {kib} KiB")

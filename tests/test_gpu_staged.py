@@ -99,15 +99,40 @@ def test_graph_replays(comm, orc):
         assert_parity(torch.stack([t.cpu() for t in rv]), want, f"staged replay {rep}")
 
 
-def test_hierarchical_order_is_refused(comm):
+def test_two_level_form_needs_a_workspace(comm):
+    """With a hierarchical order, the staged HB form is the two-level form,
+    whose node partials need the communicator's workspace: none, or too
+    little, is arInvalidUsage; a workspace that overlaps a rank buffer is
+    arInvalidArgument; enough of it runs the call."""
     y = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
     q = [t.data_ptr() for t in y]
     s = torch.cuda.current_stream().cuda_stream
+    need = 2 * 256  # 2 nodes x roundup(64 * 4, 256)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
     comm.set_option(ar.arOption.arOptNodeRanks, 8)
+    comm.set_option(ar.arOption.arOptHBStaged, 1)
     try:
-        assert ar.arAllReduce(q, q, 64, 0, 0, 16, 1, comm.handle, s) == ar.arResult.arUnsupported
+        note("two-level form: workspace rules")
+        assert ar.arAllReduce(q, q, 64, 0, 0, 16, 1, comm.handle, s) == \
+            ar.arResult.arInvalidUsage
+        assert ar.arCommSetWorkspace(comm.handle, ws.data_ptr(), need - 1) == \
+            ar.arResult.arSuccess
+        assert ar.arAllReduce(q, q, 64, 0, 0, 16, 1, comm.handle, s) == \
+            ar.arResult.arInvalidUsage
+        assert ar.arCommSetWorkspace(comm.handle, y.data_ptr(), need) == ar.arResult.arSuccess
+        assert ar.arAllReduce(q, q, 64, 0, 0, 16, 1, comm.handle, s) == \
+            ar.arResult.arInvalidArgument
+        assert ar.arCommSetWorkspace(comm.handle, ws.data_ptr() + 16, need) == \
+            ar.arResult.arInvalidArgument
+        assert ar.arCommSetWorkspace(comm.handle, ws.data_ptr(), 0) == \
+            ar.arResult.arInvalidArgument
+        assert ar.arCommSetWorkspace(comm.handle, ws.data_ptr(), need) == ar.arResult.arSuccess
+        assert ar.arAllReduce(q, q, 64, 0, 0, 16, 1, comm.handle, s) == ar.arResult.arSuccess
+        torch.cuda.synchronize()
     finally:
         comm.set_option(ar.arOption.arOptNodeRanks, 0)
+        comm.set_option(ar.arOption.arOptHBStaged, 0)
+        assert ar.arCommSetWorkspace(comm.handle, None, 0) == ar.arResult.arSuccess
     assert ar.arAllReduce(q, q, 64, 0, 0, 16, 1, comm.handle, s) == ar.arResult.arSuccess
     torch.cuda.synchronize()
     with pytest.raises(ar.ArError):
