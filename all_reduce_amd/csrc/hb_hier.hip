@@ -58,6 +58,8 @@ constexpr int kHierMaxThreads = 512;
 template <typename T>
 constexpr int per_vec() { return 16 / T::kBytes; }
 
+__device__ inline float as_float(uint32_t w) { return __builtin_bit_cast(float, w); }
+
 template <typename T>
 __device__ inline float tail_load(const void *base, uint64_t i)
 {
@@ -164,16 +166,19 @@ __global__ __launch_bounds__(kHierMaxThreads) void hb_hier_fold(HierParams p)
 #pragma unroll
                 for (int h = 0; h < H; ++h)
                     pv[g][h] = load16<NT>((const u32x4 *)(p.ws + g * p.pstride + i * PV) + h);
+        // (each vector element goes through a uint32_t value before the bit
+        // cast: hipcc bit-casts an element of a vector-typed lvalue wrongly,
+        // reading another lane)
         float total[PV];
 #pragma unroll
         for (int e = 0; e < PV; ++e)
-            total[e] = __builtin_bit_cast(float, pv[0][e / 4][e % 4]);
+            total[e] = as_float(pv[0][e / 4][e % 4]);
 #pragma unroll
         for (int g = 1; g < GMAX; ++g)
             if (GC > 0 || g < (int)G)
 #pragma unroll
                 for (int e = 0; e < PV; ++e)
-                    total[e] = total[e] + __builtin_bit_cast(float, pv[g][e / 4][e % 4]);
+                    total[e] = total[e] + as_float(pv[g][e / 4][e % 4]);
         u32x4 y;
 #pragma unroll
         for (int q = 0; q < 4; ++q)

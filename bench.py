@@ -100,6 +100,9 @@ def parse():
     ap.add_argument("--tune", action="store_true",
                     help="run the start-up tuning (arCommTune) first, as SGLang's integration "
                          "does; by default the built-in launch shapes are timed")
+    ap.add_argument("--sizes", default=None,
+                    help="with --only ll_variants: comma-separated log2 element counts to run "
+                         "(default: the whole sweep, 10..19)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle checks")
     return ap.parse_args()
@@ -493,7 +496,7 @@ def main():
     if args.only == "ll_variants":
         opt = B.ar.arOption
         rows = []
-        for k in SWEEP:
+        for k in ([int(v) for v in args.sizes.split(",")] if args.sizes else SWEEP):
             case = inputs.sweep(k)
             n = case["count"]
             x = inputs.make(**case)

@@ -148,22 +148,21 @@ def test_c5b_two_level_full_size(comm, orc, R, inplace):
 
 def test_two_level_in_graph_replays(comm, orc):
     """Captured calls replay correctly with new inputs between replays (the
-    workspace is reused by every call)."""
+    workspace is reused by every call).  The prepared call is made inside the
+    capture, so it is bound to the capturing stream."""
     R, N, group = 16, 50_003, 4
     _, sv = ar.rank_buffers(R, N, torch.bfloat16, comm.device)
     plane, rv = ar.rank_buffers(R, N, torch.bfloat16, comm.device)
+    g = torch.cuda.CUDAGraph()
     with two_level(comm, group):
-        call = comm.prepare(sv, rv, "hb")
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            call()
-        torch.cuda.current_stream().wait_stream(s)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            comm.prepare(sv, rv, "hb")()
+        torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-    with two_level(comm, group):
-        call = comm.prepare(sv, rv, "hb")
         with torch.cuda.graph(g):
+            call = comm.prepare(sv, rv, "hb")
             call()
             call()
     for rep, seed in enumerate((601, 602, 603)):
@@ -171,6 +170,7 @@ def test_two_level_in_graph_replays(comm, orc):
         for r in range(R):
             sv[r].copy_(x[r])
         plane.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
         note(f"two-level graph replay {rep}")
         g.replay()
         torch.cuda.synchronize()
