@@ -64,6 +64,7 @@ class arOption(IntEnum):
 
 
 AR_MAX_RANKS = 32
+AR_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class arTunedShape(ctypes.Structure):
@@ -111,6 +112,8 @@ def library() -> ctypes.CDLL:
         "arCommGetTunedShape": ([vp, i32, i32, i32, sz, i32, ctypes.POINTER(arTunedShape)], i32),
         "arCommGetLastLaunch": ([vp, ctypes.POINTER(arLaunchInfo)], i32),
         "arCommSetWorkspace": ([vp, vp, sz], i32),
+        "arAllReduceNoAlloc": ([ctypes.POINTER(vp), ctypes.POINTER(vp), sz, i32, i32, i32, i32,
+                                vp], i32),
         "arGetErrorString": ([i32], ctypes.c_char_p),
         "arGetVersion": ([], i32),
     }
@@ -205,6 +208,16 @@ def arAllReduce(sendbufs: Sequence[int] | None, recvbufs: Sequence[int] | None, 
     d = _pointer_array(recvbufs, nranks)
     return library().arAllReduce(s, d, count, int(dtype), int(op), nranks, int(protocol),
                                  comm, stream)
+
+
+def arAllReduceNoAlloc(sendbufs: Sequence[int] | None, recvbufs: Sequence[int] | None,
+                       count: int, dtype: int, op: int, nranks: int, node_ranks: int,
+                       stream) -> int:
+    """Device pointers as integers; ``None`` passes a NULL array."""
+    s = _pointer_array(sendbufs, nranks)
+    d = _pointer_array(recvbufs, nranks)
+    return library().arAllReduceNoAlloc(s, d, count, int(dtype), int(op), nranks,
+                                        int(node_ranks), stream)
 
 
 # ---- torch conveniences ---------------------------------------------------

@@ -17,10 +17,18 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
 #include "ar_internal.hpp"
+
+// Device scratch of arAllReduceNoAlloc: the node partials of its staged
+// two-level form, one copy per GPU, held until the process ends.  In host
+// code `scratch` is only a stand-in for the symbol: its device address is
+// looked up once per device with hipGetSymbolAddress (noalloc_device below)
+// and only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[AR_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -276,6 +284,38 @@ int hierarchy_group(const arComm *comm, int nranks)
 {
     const int g = (int)comm->opt[arOptNodeRanks];
     return g > 1 && g < nranks ? g : 0;
+}
+
+// Per-device state of arAllReduceNoAlloc: the device address of `scratch` and
+// the compute-unit count, found once per device with that device current.
+// Neither lookup allocates.
+constexpr int kNoAllocMaxDevices = 64;
+struct NoAllocDevice {
+    bool ready;
+    void *scratch;
+    int cu_count;
+};
+std::mutex g_noalloc_mu;
+NoAllocDevice g_noalloc[kNoAllocMaxDevices];
+
+arResult_t noalloc_device(int device, NoAllocDevice *out)
+{
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    NoAllocDevice &d = g_noalloc[device];
+    if (!d.ready) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+            return reject(arHipError, "hipGetSymbolAddress of the no-alloc scratch failed");
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) !=
+                hipSuccess || cus <= 0)
+            return reject(arHipError, "device attribute query failed");
+        d.scratch = ptr;
+        d.cu_count = cus;
+        d.ready = true;
+    }
+    *out = d;
+    return arSuccess;
 }
 
 // RAII restore of the caller's current device.
@@ -726,6 +766,45 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype_arg, int nranks,
             result = reject(arTimeout, "an LL wait timed out while tuning");
     }
     return result;
+}
+
+arResult_t arAllReduceNoAlloc(const void *const *sendbufs, void *const *recvbufs, size_t count,
+                              arDataType_t dtype_arg, arRedOp_t op_arg, int nranks,
+                              int nodeRanks, arStream_t stream)
+{
+    arResult_t r = validate(sendbufs, recvbufs, count, raw(dtype_arg), raw(op_arg), nranks,
+                            arProtoHB);
+    if (r != arSuccess)
+        return r;
+    if (nodeRanks < 0 || nodeRanks > AR_MAX_RANKS)
+        return reject(arInvalidArgument, "nodeRanks must be in 0..32");
+    if (count == 0)
+        return arSuccess;
+    const int group = nodeRanks > 1 && nodeRanks < nranks ? nodeRanks : 0;
+    if (group != 0 && nranks % group != 0)
+        return reject(arInvalidUsage, "nranks is not a multiple of nodeRanks");
+    if (group != 0 &&
+        ar::hier_workspace_bytes(count, nranks / group) > (uint64_t)AR_NOALLOC_SCRATCH_BYTES)
+        return reject(arInvalidUsage, "the node partials exceed AR_NOALLOC_SCRATCH_BYTES");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices)
+        return reject(arHipError, "no usable current device");
+    NoAllocDevice d = {};
+    r = noalloc_device(dev, &d);
+    if (r != arSuccess)
+        return r;
+    // The HB defaults: 256 threads, one workgroup per CU, non-temporal
+    // accesses, interleaved chunks; no launch record.
+    const ar::HBConfig cfg = {d.cu_count, 1, true, nullptr};
+    const int dtype = raw(dtype_arg);
+    const hipError_t e =
+        group != 0 ? ar::launch_hb_hier(sendbufs, recvbufs, count, dtype, nranks, group, d.scratch,
+                                        cfg, 0, 0, true, (hipStream_t)stream)
+                   : ar::launch_hb(sendbufs, recvbufs, count, dtype, nranks, cfg, 0, 0, 0, true,
+                                   (hipStream_t)stream);
+    if (e != hipSuccess)
+        return reject(arHipError, hipGetErrorString(e));
+    return arSuccess;
 }
 
 arResult_t arCommGetLastLaunch(arComm_t comm, arLaunchInfo_t *info)

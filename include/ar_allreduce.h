@@ -376,6 +376,37 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
                        arDataType_t dtype, arRedOp_t op, int nranks, arProtocol_t protocol,
                        arComm_t comm, arStream_t stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc -- and so
+ * cannot create a communicator: the HB all-reduce with no communicator and
+ * no allocation of any kind.
+ *
+ * nodeRanks 0, 1 or >= nranks: the fused HB two-shot in the flat order
+ * 0..R-1 (no scratch).  1 < nodeRanks < nranks: the staged two-level form
+ * of arOptHBStaged with arOptNodeRanks = nodeRanks (node partials, a kernel
+ * boundary, the fold across nodes), same bits as arAllReduce there, with
+ * the node partials in a scratch array that the library holds in device
+ * memory, one per GPU it runs on, for the life of the process:
+ * AR_NOALLOC_SCRATCH_BYTES (64 MiB), so (nranks / nodeRanks) *
+ * roundup(count * 4, 256) bytes must fit (else arInvalidUsage; larger
+ * messages take arAllReduce with a workspace).  Nothing in the scratch needs
+ * to start at any value: every call writes the partials it reads.
+ *
+ * Runs on the current device with the HB defaults (256 threads, one
+ * workgroup per compute unit, non-temporal accesses, interleaved chunks).
+ * The arguments and their rules are arAllReduce's (protocol HB); nodeRanks
+ * outside 0..32 is arInvalidArgument, a nodeRanks in between that does not
+ * divide nranks arInvalidUsage.  The first call on a device looks up the
+ * scratch's address and the device's compute units (no allocation).
+ * All calls on one GPU share its scratch, which keeps the last call's
+ * contents: two two-level calls that overlap in time on one GPU (on streams
+ * with no ordering between them) race, and their results are undefined.
+ * Calls on one stream, or captured into one graph, are ordered and safe. */
+#define AR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+arResult_t arAllReduceNoAlloc(const void *const *sendbufs, void *const *recvbufs, size_t count,
+                              arDataType_t dtype, arRedOp_t op, int nranks, int nodeRanks,
+                              arStream_t stream);
+
 /* Static description of a result code (arUnsupported is the guide's
  * "fall back to another all-reduce", sections 4.3 and 5). */
 const char *arGetErrorString(arResult_t result);

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     lib = ar.library()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
@@ -40,6 +40,8 @@ def test_enums_match_header():
             m = re.search(rf"\b{member.name}\s*=\s*(\d+)", HEADER)
             assert m and int(m.group(1)) == member.value, member
     assert int(re.search(r"#define AR_MAX_RANKS (\d+)", HEADER).group(1)) == ar.AR_MAX_RANKS
+    m = re.search(r"#define AR_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", HEADER)
+    assert int(m.group(1)) << int(m.group(2)) == ar.AR_NOALLOC_SCRATCH_BYTES
 
 
 def test_version_and_error_strings():
