@@ -61,6 +61,7 @@ class arOption(IntEnum):
     arOptLLFlagScheme = 12
     arOptDebugSeqStart = 13
     arOptTuneFreshInputs = 14
+    arOptLLDense = 15
 
 
 AR_MAX_RANKS = 32
@@ -79,7 +80,7 @@ class arLaunchInfo(ctypes.Structure):
     _fields_ = [("protocol", ctypes.c_int), ("kernels", ctypes.c_int), ("grid", ctypes.c_uint),
                 ("threads", ctypes.c_uint), ("packetBytes", ctypes.c_int),
                 ("nonTemporal", ctypes.c_int), ("nodeRanks", ctypes.c_int),
-                ("staged", ctypes.c_int)]
+                ("staged", ctypes.c_int), ("packetPayloadBytes", ctypes.c_int)]
 
 
 class ArError(RuntimeError):

@@ -93,6 +93,7 @@ constexpr int64_t kDefaults[kOptionCount] = {
     0,        // arOptLLFlagScheme (cleared)
     0,        // arOptDebugSeqStart
     0,        // arOptTuneFreshInputs (unchanged inputs)
+    -1,       // arOptLLDense (by size)
 };
 
 // Argument checks shared by every protocol.  No HIP call.
@@ -178,11 +179,27 @@ ar::HBConfig hb_config(const arComm *comm)
             &comm->last};
 }
 
+// Whether an LL call takes the three-element packets (ll_dense.hip): 16-bit
+// types in the flat order, the cleared scheme and 8-byte packets only; then
+// arOptLLDense, or by default from the size where they measured faster.
+bool ll_dense(const arComm *comm, arDataType_t dtype, int nranks, size_t bytes, int pkt_bytes,
+              int scheme, int group)
+{
+    if (dtype == arFloat32 || group != 0 || scheme != ar::kSchemeCleared || pkt_bytes == 16)
+        return false;
+    const int64_t o = comm->opt[arOptLLDense];
+    return o < 0 ? bytes >= ar::ll_dense_from_bytes(nranks) : o == 1;
+}
+
 hipError_t launch(const void *const *send, void *const *recv, size_t count, arDataType_t dtype,
                   int nranks, arProtocol_t proto, const arComm *comm, int threads,
                   uint64_t blocks, int pkt_bytes, int scheme, int group, bool nt,
                   hipStream_t stream)
 {
+    if (proto == arProtoLL && ll_dense(comm, dtype, nranks, count * elem_bytes(dtype), pkt_bytes,
+                                       scheme, group))
+        return ar::launch_ll_dense(send, recv, count, (int)dtype, nranks, comm, threads, blocks,
+                                   stream);
     return proto == arProtoLL
                ? ar::launch_ll(send, recv, count, (int)dtype, nranks, comm, threads, blocks,
                                pkt_bytes, scheme, group, stream)
@@ -379,7 +396,7 @@ arResult_t arCommCreate(arComm_t *comm, int device, int maxRanks, size_t maxLLBy
     c->max_ranks = maxRanks;
     c->max_ll_bytes = maxLLBytesPerRank;
     memcpy(c->opt, kDefaults, sizeof(kDefaults));
-    c->last = {-1, 0, 0, 0, 0, 0, 0, 0};
+    c->last = {-1, 0, 0, 0, 0, 0, 0, 0, 0};
     c->ws = nullptr;
     c->ws_bytes = 0;
 
@@ -494,6 +511,7 @@ arResult_t arCommSetOption(arComm_t comm, arOption_t option_arg, int64_t value)
     case arOptLLFlagScheme: ok = value == 0 || value == 1; break;
     case arOptDebugSeqStart: ok = value >= 0 && value <= 0xffffffffLL; break;
     case arOptTuneFreshInputs: ok = value == 0 || value == 1; break;
+    case arOptLLDense: ok = value >= -1 && value <= 1; break;
     case arOptLLPacketBytes:
         if (value == 16 && !comm->ll16_ok)
             return reject(arUnsupported, "16-byte packets need packet memory below 4 GiB");
@@ -598,7 +616,8 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
     // else non-temporal.
     int nt = (int)comm->opt[arOptHBNonTemporal];
     const ar::TunedShape &t = comm->tuned[dtype][nranks][proto][in_place][bucket_of(bytes)];
-    if (threads == 0 && blocks == 0 && pkt == 0 && scheme == ar::kSchemeCleared && t.valid) {
+    if (threads == 0 && blocks == 0 && pkt == 0 && scheme == ar::kSchemeCleared &&
+        comm->opt[arOptLLDense] < 0 && t.valid) {
         threads = t.threads;
         blocks = (uint64_t)t.blocks;
         pkt = t.pkt_bytes;
@@ -817,6 +836,7 @@ arResult_t arCommGetLastLaunch(arComm_t comm, arLaunchInfo_t *info)
     info->grid = l.grid;
     info->threads = l.threads;
     info->packetBytes = l.pkt_bytes;
+    info->packetPayloadBytes = l.payload;
     info->nonTemporal = l.nt;
     info->nodeRanks = l.node;
     info->staged = l.staged;

@@ -48,6 +48,51 @@ inline LLShape ll_default_shape(int nranks, uint64_t bytes_per_rank)
     return kTable[nranks <= 8 ? 0 : (nranks <= 16 ? 1 : 2)][s];
 }
 
+// The same for the three-element packets of bfloat16 and float16 (ll_dense.hip),
+// from the size per rank where they are the default packet (ll_dense_from_bytes;
+// below it the entries are unused): measured on MI355X like the word table,
+// 64-512 threads, 1-128 workgroups per rank (the occupancy cap applies).
+inline LLShape ll_dense_default_shape(int nranks, uint64_t bytes_per_rank)
+{
+    static constexpr LLShape kTable[3][10] = {
+        // 2K        4K        8K        16K       32K        64K
+        // 128K      256K       512K       1M
+        {{256, 1}, {256, 2}, {256, 4}, {256, 8}, {256, 16}, {256, 32},
+         {256, 64}, {64, 128}, {256, 64}, {256, 128}},
+        {{512, 1}, {512, 1}, {512, 2}, {512, 4}, {256, 8}, {256, 32},
+         {256, 32}, {128, 128}, {256, 64}, {256, 64}},
+        {{512, 1}, {512, 1}, {512, 1}, {512, 2}, {512, 4}, {512, 8},
+         {256, 16}, {128, 128}, {128, 128}, {512, 64}},
+    };
+    int s = 0;
+    while (s < 9 && ((uint64_t)2048 << s) < bytes_per_rank)
+        ++s;
+    return kTable[nranks <= 8 ? 0 : (nranks <= 16 ? 1 : 2)][s];
+}
+
+// Bytes per rank from which three-element packets are the default: measured
+// on MI355X, they cost about 0.5 us of LDS staging per call at small sizes and
+// win from 256 KiB per rank at 8 ranks (1 MiB: 7.95 against 9.79 us) and from
+// 128 KiB at 32 (1 MiB: 28.5 against 37.7 us).
+inline uint64_t ll_dense_from_bytes(int nranks)
+{
+    return nranks <= 16 ? ((uint64_t)256 << 10) : ((uint64_t)128 << 10);
+}
+
+// Default threads per workgroup of the fused HB kernel (one workgroup per
+// CU), by rank count and message size per rank, measured on MI355X: 256 up to
+// 8 ranks; from 9 to 16 ranks 128 up to 16 MiB per rank (2^18 fp16 at 16
+// ranks: 4.2 against 5.1 us with 256) and 64 above (4096 x 7168 fp32: 671
+// against 689 us); 128 from 17 ranks.
+inline int hb_default_threads(int nranks, uint64_t bytes_per_rank)
+{
+    if (nranks <= 8)
+        return 256;
+    if (nranks <= 16)
+        return bytes_per_rank <= ((uint64_t)16 << 20) ? 128 : 64;
+    return 128;
+}
+
 // LL flag schemes (the values of arOptLLFlagScheme): the reader zeroes each
 // consumed packet (the default), or each 512-byte packet group carries a
 // sequence number.
@@ -62,8 +107,11 @@ constexpr int kNodeMask = -1;
 
 // LL kernel kinds with their own occupancy: the cleared scheme in the flat
 // order, the sequenced scheme (flat order only), then the cleared scheme in
-// the hierarchical order with a node bitmask, or with nodes of 2, 4, 8 or 16.
-constexpr int kLLKinds = 7;
+// the hierarchical order with a node bitmask, or with nodes of 2, 4, 8 or 16,
+// and last the three-element packets (ll_dense.hip; 16-bit types, flat order,
+// cleared scheme, packet-width index 0).
+constexpr int kLLKinds = 8;
+constexpr int kLLDenseKind = 7;
 constexpr int ll_kind(bool seq, int node)
 {
     return node == kNodeFlat ? (seq ? 1 : 0)
@@ -73,7 +121,7 @@ constexpr int ll_kind(bool seq, int node)
 
 }  // namespace ar
 
-constexpr int kOptionCount = 15;
+constexpr int kOptionCount = 16;
 
 namespace ar {
 // One tuned launch shape: threads per workgroup and workgroups (HB: the
@@ -100,6 +148,8 @@ struct LaunchRecord {
     int32_t nt;         // HB: non-temporal accesses (LL: 0)
     int32_t node;       // ranks per node of a hierarchical order, else 0
     int32_t staged;     // HB: 1 for a staged form (kernel boundary between shots)
+    int32_t payload;    // LL payload bytes per packet: 4 and 8 (word packets of 8 and
+                        // 16 bytes), 6 (three 16-bit elements); HB: 0
 };
 }  // namespace ar
 
@@ -187,6 +237,13 @@ inline uint64_t hier_workspace_bytes(uint64_t count, int nodes)
 {
     return hier_partial_stride(count) * (uint64_t)nodes;
 }
+// The LL one-shot with three-element packets (bfloat16 / float16 only, flat
+// order, cleared scheme, 8-byte packets).
+hipError_t launch_ll_dense(const void *const *send, void *const *recv, size_t count, int dtype,
+                           int nranks, const arComm *comm, int threads, uint64_t blocks,
+                           hipStream_t stream);
+// Its occupancy table, [dtype][rank variant][thread-count index].
+hipError_t query_ll_dense_residency(int (*per_cu)[kRankVariants + 1][kThreadChoices]);
 // Zeroes the packets and the error word and sets the sequence table to
 // arOptDebugSeqStart (0 by default).
 hipError_t launch_reset(const arComm *comm, hipStream_t stream);

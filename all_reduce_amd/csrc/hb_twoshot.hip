@@ -259,9 +259,10 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     int u = cfg.unroll > 0 ? cfg.unroll : 1;
     if (u > max_unroll(RMAX))
         u = max_unroll(RMAX);
-    // Default: 256 threads (128 from 32 ranks up), one workgroup per CU --
-    // measured on MI355X, fewer loads in flight per CU stream HBM faster.
-    uint32_t threads = want_threads > 0 ? (uint32_t)want_threads : (nranks >= 32 ? 128u : 256u);
+    // Default: one workgroup per CU -- measured on MI355X, fewer loads in
+    // flight per CU stream HBM faster -- of hb_default_threads threads.
+    uint32_t threads = want_threads > 0 ? (uint32_t)want_threads
+                                        : (uint32_t)hb_default_threads(nranks, count * T::kBytes);
     if (threads > (uint32_t)hb_max_threads(RMAX))
         threads = (uint32_t)hb_max_threads(RMAX);
     const uint64_t blocks = want_blocks > 0 ? want_blocks : (uint64_t)cfg.cu_count;

@@ -483,7 +483,7 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     const uint32_t grid = (uint32_t)(per_rank * (uint64_t)nranks);
 
     comm->last = {arProtoLL, 1, grid, (uint32_t)threads, 8 * PW, 0,
-                  NODE == kNodeFlat ? 0 : group, 0};
+                  NODE == kNodeFlat ? 0 : group, 0, 4 * PW};
     hipLaunchKernelGGL((ll_oneshot<T, RMAX, EXACT, PW, SEQ, NODE>), dim3(grid), dim3(threads), 0,
                        stream, p);
     return hipGetLastError();
@@ -678,6 +678,7 @@ hipError_t query_ll_residency(arComm *comm)
     if ((e = query_grouped<4>(per_cu[ll_kind(false, 4)])) != hipSuccess) return e;
     if ((e = query_grouped<8>(per_cu[ll_kind(false, 8)])) != hipSuccess) return e;
     if ((e = query_grouped<16>(per_cu[ll_kind(false, 16)])) != hipSuccess) return e;
+    if ((e = query_ll_dense_residency(per_cu[kLLDenseKind][0])) != hipSuccess) return e;
     for (int s = 0; s < kLLKinds; ++s)
         for (int w = 0; w < 2; ++w)
             for (int d = 0; d < 3; ++d)

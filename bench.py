@@ -226,7 +226,7 @@ class Bench:
     def launch_record(self, protocol):
         """The launch shape of the communicator's last call, for the line."""
         rec = self.comm.last_launch()
-        keys = ("grid", "threads", "packetBytes") if protocol == "ll" else \
+        keys = ("grid", "threads", "packetBytes", "packetPayloadBytes") if protocol == "ll" else \
             ("grid", "threads", "nonTemporal", "kernels")
         return {k: rec[k] for k in keys}
 
@@ -491,6 +491,7 @@ def main():
                     "the read-only and write-only ceilings for equal bytes"}
         if args.only == "ceilings":
             result["ceilings"] = ceil
+        result["hbm_ceilings_c5b"] = run_c5b_ceilings(B, args)
 
     # ---- LL flag scheme x packet width at the default shape, over the sweep ---
     if args.only == "ll_variants":
@@ -871,6 +872,10 @@ def run_ceilings(B, args):
     lib.hbm_ceiling_run.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), vp, ctypes.c_uint64,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     lib.hbm_ceiling_run.restype = ctypes.c_int
+    lib.hbm_ceiling_run_n.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), vp, ctypes.c_uint64,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.hbm_ceiling_run_n.restype = ctypes.c_int
+    B.ceiling_lib = lib
     R, n = 8, 8192 * 8192                      # bf16 elements per rank: 128 MiB
     nvec = n * 2 // 16
     src = torch.empty((R, n), dtype=torch.bfloat16, device=B.dev).normal_()
@@ -933,6 +938,82 @@ def run_ceilings(B, args):
         log(f"{name}: {us:.1f} us, {out[name]['gbps']:.0f} GB/s")
     del src, dst, sink
     return out
+
+
+def run_c5b_ceilings(B, args):
+    """The C5b shape's memory ceilings: R = 16 and 32 streams of 112 MiB
+    (fp32 4096 x 7168 per rank) read only, written only (non-temporal or
+    ordinary stores), and copied out of place (2R streams, HB's access shape
+    at that R), with HB's tile mapping, best of a few launch shapes; HB itself
+    out of place on the same planes at its default shape.  GB/s counts the
+    bytes each pattern must move."""
+    import ctypes
+    torch, ar = B.torch, B.ar
+    lib = B.ceiling_lib
+    n = 4096 * 7168
+    nvec = n * 4 // 16
+    shapes = [(256, 256), (512, 256), (1024, 256), (256, 128), (512, 128), (256, 512)]
+    out = {}
+    for R in (16, 32):
+        src = torch.empty((R, n), dtype=torch.float32, device=B.dev).normal_()
+        dst = torch.empty_like(src)
+        sink = torch.empty(max(g * t for g, t in shapes) * 4, dtype=torch.int32, device=B.dev)
+        sp = (ctypes.c_void_p * R)(*[src[j].data_ptr() for j in range(R)])
+        dp = (ctypes.c_void_p * R)(*[dst[j].data_ptr() for j in range(R)])
+        one = R * n * 4
+        res = {}
+        for name, mode, d, nbytes in (("read", 0, sp, one), ("write", 1, dp, one),
+                                      ("write, ordinary stores", 3, dp, one),
+                                      ("copy out of place", 2, dp, 2 * one)):
+            best = 0.0
+            # the probe holds R vectors per lane: at most 512 threads at 16
+            # streams and 256 at 32, as the HB kernel
+            for g, t in [(g, t) for g, t in shapes if t <= (256 if R >= 32 else 512)]:
+                def fn(mode=mode, d=d, g=g, t=t):
+                    rc = lib.hbm_ceiling_run_n(sp, d, sink.data_ptr(), nvec, mode, g, t, R,
+                                               torch.cuda.current_stream().cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError("hbm_ceiling_run_n refused its launch")
+                us = _timed(B, fn, args.steps)
+                best = max(best, nbytes / (us * 1e-6) / 1e9)
+            res[name] = round(best, 1)
+        srcs = [src[j].data_ptr() for j in range(R)]
+        dsts = [dst[j].data_ptr() for j in range(R)]
+
+        def hb():
+            rc = ar.arAllReduce(srcs, dsts, n, ar.arDataType.arFloat32, ar.arRedOp.arSum, R,
+                                ar.arProtocol.arProtoHB, B.comm.handle,
+                                torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise ar.ArError(rc, "arAllReduce")
+        hb_gbps = 2 * one / (_timed(B, hb, args.steps) * 1e-6) / 1e9
+        wr = max(res["write"], res["write, ordinary stores"])
+        bound = 2.0 / (1.0 / res["read"] + 1.0 / wr)
+        out[f"r{R}"] = {"read_gbps": res["read"], "write_gbps": wr,
+                        "copy_out_of_place_gbps": res["copy out of place"],
+                        "read_write_bound_gbps": round(bound, 1),
+                        "hb_out_of_place_gbps": round(hb_gbps, 1),
+                        "hb_frac_of_peak": round(hb_gbps / HBM_PEAK_GBPS, 4),
+                        "hb_frac_of_copy": round(hb_gbps / res["copy out of place"], 4),
+                        "hb_frac_of_read_write_bound": round(hb_gbps / bound, 4)}
+        log(f"C5b ceilings R={R}: read {res['read']:.0f}, write {wr:.0f}, copy out of place "
+            f"{res['copy out of place']:.0f}, read/write bound {bound:.0f}; HB {hb_gbps:.0f} GB/s "
+            f"({100 * hb_gbps / res['copy out of place']:.1f}% of the copy)")
+        del src, dst, sink
+    return out
+
+
+def _timed(B, fn, reps):
+    for _ in range(2):
+        fn()
+    B.torch.cuda.synchronize()
+    t0, t1 = B.events()
+    t0.record()
+    for _ in range(reps):
+        fn()
+    t1.record()
+    B.torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1000.0 / reps
 
 
 def _sources_digest() -> str:

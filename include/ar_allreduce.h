@@ -110,7 +110,9 @@ typedef enum {
      * message size. */
     arOptLLThreads = 6,
     /* HB: threads per workgroup (64 .. 1024, a multiple of 64; capped at 512
-     * above 8 ranks and 256 above 16); 0 = default (256, or 128 from 32 ranks). */
+     * above 8 ranks and 256 above 16); 0 = default (256 up to 8 ranks; 128
+     * from 9 to 16 ranks up to 16 MiB per rank and 64 above; 128 from 17
+     * ranks: the fastest measured on MI355X at the configured sizes). */
     arOptHBThreads = 7,
     /* HB: which elements simulated rank c reduces (its chunk) -- 0: the
      * contiguous c-th of R equal parts, 1: every R-th tile starting at tile c
@@ -185,7 +187,20 @@ typedef enum {
      * message), as when every step of a model produces new inputs; the
      * rewrites' own time, measured alone, is subtracted.  On MI355X this
      * changes the HB access policy that wins from a few MiB per rank up. */
-    arOptTuneFreshInputs = 14
+    arOptTuneFreshInputs = 14,
+    /* LL, bfloat16 and float16: the packet format.  1: three elements and a
+     * 16-bit flag in each 8-byte packet (48 bits of payload, still one 64-bit
+     * atomic store, so a reader that sees the flag sees the elements): a
+     * third fewer packet and clear bytes than the word packet, whose
+     * 4-byte payload sits next to a 4-byte flag.  0: the word packet.
+     * -1 (default): three-element packets from the size where they measured
+     * faster on MI355X (256 KiB per rank up to 16 ranks, 128 KiB above),
+     * word packets below, where their LDS staging costs more than the bytes
+     * they save.
+     * Applies to the flat order, the cleared flag scheme and 8-byte packets;
+     * float32, arOptNodeRanks, the sequenced scheme and 16-byte packets use
+     * word packets.  A value other than -1 also turns the tuned LL entry off. */
+    arOptLLDense = 15
 } arOption_t;
 
 /* The communicator is the long-lived group resource of an NCCL-style
@@ -335,6 +350,8 @@ typedef struct {
     int nonTemporal;   /* HB: 1 non-temporal accesses, 0 cached; LL: 0 */
     int nodeRanks;     /* ranks per node of a hierarchical order; 0: flat */
     int staged;        /* HB: 1 for a staged form; else 0 */
+    int packetPayloadBytes; /* LL: payload bytes per packet -- 4 (8-byte word packet),
+                             * 6 (three 16-bit elements), 8 (16-byte packet); HB: 0 */
 } arLaunchInfo_t;
 
 /* Copy the record of the most recent launch to *info.  Returns

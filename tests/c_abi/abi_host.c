@@ -30,12 +30,12 @@ int main(int argc, char **argv)
                offsetof(arTunedShape_t, packetBytes), offsetof(arTunedShape_t, nonTemporal),
                offsetof(arTunedShape_t, us));
         printf("arLaunchInfo_t %zu protocol %zu kernels %zu grid %zu threads %zu "
-               "packetBytes %zu nonTemporal %zu nodeRanks %zu staged %zu\n",
+               "packetBytes %zu nonTemporal %zu nodeRanks %zu staged %zu packetPayloadBytes %zu\n",
                sizeof(arLaunchInfo_t), offsetof(arLaunchInfo_t, protocol),
                offsetof(arLaunchInfo_t, kernels), offsetof(arLaunchInfo_t, grid),
                offsetof(arLaunchInfo_t, threads), offsetof(arLaunchInfo_t, packetBytes),
                offsetof(arLaunchInfo_t, nonTemporal), offsetof(arLaunchInfo_t, nodeRanks),
-               offsetof(arLaunchInfo_t, staged));
+               offsetof(arLaunchInfo_t, staged), offsetof(arLaunchInfo_t, packetPayloadBytes));
         printf("arResult_t %zu arDataType_t %zu arRedOp_t %zu arProtocol_t %zu arOption_t %zu\n",
                sizeof(arResult_t), sizeof(arDataType_t), sizeof(arRedOp_t),
                sizeof(arProtocol_t), sizeof(arOption_t));

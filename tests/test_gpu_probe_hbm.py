@@ -33,6 +33,9 @@ def probe():
     lib.hbm_ceiling_run.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), vp, ctypes.c_uint64,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     lib.hbm_ceiling_run.restype = ctypes.c_int
+    lib.hbm_ceiling_run_n.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), vp, ctypes.c_uint64,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.hbm_ceiling_run_n.restype = ctypes.c_int
     return lib
 
 
@@ -96,3 +99,35 @@ def test_read_folds_every_vector(probe):
 def test_bad_launch_shapes_are_refused(probe, grid, threads, mode):
     _, src = _planes()
     assert _run(probe, src, src, None, mode, grid, threads) == -1
+
+
+@pytest.mark.parametrize("streams", [16, 32])
+def test_more_streams_out_of_place_copy_and_read(probe, streams):
+    """The 16- and 32-stream forms (the R = 16 / 32 workloads' shapes): an
+    out-of-place copy moves every vector of every stream, and a read folds
+    every vector into the sink."""
+    g = torch.Generator().manual_seed(8)
+    host = torch.randint(-2**31, 2**31 - 1, (streams, NVEC * 4), generator=g,
+                         dtype=torch.int64).to(torch.int32)
+    src = host.cuda()
+    dst = torch.zeros_like(src)
+    vp = ctypes.c_void_p
+    sp = (vp * streams)(*[src[j].data_ptr() for j in range(streams)])
+    dp = (vp * streams)(*[dst[j].data_ptr() for j in range(streams)])
+    grid = 4 * streams
+    note(f"hbm ceiling probe {streams} streams: copy out of place, read")
+    assert probe.hbm_ceiling_run_n(sp, dp, None, NVEC, 2, grid, THREADS, streams,
+                                   torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dst.cpu(), host)
+    sink = torch.zeros(grid * THREADS * 4, dtype=torch.int32, device="cuda")
+    assert probe.hbm_ceiling_run_n(sp, sp, sink.data_ptr(), NVEC, 0, grid, THREADS, streams,
+                                   torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32).reshape(-1, 4), axis=0)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32).reshape(-1, 4), axis=0)
+    assert np.array_equal(got, want)
+    for bad_streams, bad_grid, bad_threads in ((streams, grid + 1, THREADS), (12, grid, THREADS),
+                                               (streams, grid, 1024)):
+        assert probe.hbm_ceiling_run_n(sp, dp, None, NVEC, 2, bad_grid, bad_threads, bad_streams,
+                                       torch.cuda.current_stream().cuda_stream) == -1
