@@ -13,8 +13,9 @@ section 4.4, arCommTune for bf16 R = 8 up to 128 MiB per rank):
   MSCCL++ All-Reduce 基准测试与推理集成指南", blog.gitcode.com, section 3.3):
   10 calls captured in one graph, ``--warmup`` untimed replays, then
   ``--steps`` replays inside one HIP event pair; latency per call = elapsed /
-  (steps * 10).  One untimed pass over every size and protocol comes first,
-  so no size is timed as the first use of anything; four more timed passes
+  (steps * 10).  Untimed passes over every size and protocol come first (for
+  at least 2 s), so no size is timed as the first use of anything, nor while
+  the GPU comes out of idle; four more timed passes
   per size give a median beside the guide's figure.  Each size also gets the
   guide's eager timing (2 warm-up calls, then the mean of 10 back-to-back
   calls) for LL and HB, through prepared calls (arguments marshalled once),
@@ -325,18 +326,26 @@ def main():
     # ---- LL sweep (HB, eager and plain torch at the same sizes) -------------
     sweep_rows = []
     if args.only in ("all", "sweep"):
-        # One untimed pass over every size and protocol first (graphs captured
-        # and replayed, eager calls), so that no size is timed as the first
-        # use of a buffer size, a graph shape or a kernel.
-        for k in SWEEP:
-            xw = inputs.make(**inputs.sweep(k))
-            sv, rv = B.planes(xw)
-            n = xw.shape[1]
-            for proto in ("ll", "hb"):
-                B.graph_passes(sv, rv, n, proto)
-                B.eager_us(B.comm.prepare(sv, rv, proto))
-            del sv, rv
-        torch.cuda.synchronize()
+        # Untimed passes over every size and protocol first (graphs captured
+        # and replayed, eager calls), repeated for at least 2 s, so that no
+        # size is timed as the first use of a buffer size, a graph shape or a
+        # kernel, nor while the GPU is still coming out of idle (on some
+        # machines the first timed size ran up to 1 us slow after a single
+        # short pass).
+        warm_inputs = [inputs.make(**inputs.sweep(k)) for k in SWEEP]
+        t_warm = time.perf_counter()
+        while True:
+            for xw in warm_inputs:
+                sv, rv = B.planes(xw)
+                n = xw.shape[1]
+                for proto in ("ll", "hb"):
+                    B.graph_passes(sv, rv, n, proto)
+                    B.eager_us(B.comm.prepare(sv, rv, proto))
+                del sv, rv
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_warm >= 2.0:
+                break
+        del warm_inputs
         for k in SWEEP:
             case = inputs.sweep(k)
             n = case["count"]
