@@ -60,9 +60,9 @@ share of the 8 TB/s HBM peak, HBM GB/s from the committed rocprofv3 counter
 summaries where one covers the kernel, the oracle's time at 1 and at all
 host threads and its own GB/s, parity.
 
-``--only {sweep, prefill, copy, c5, c5b, ll_variants, ceilings}`` runs one
-part alone (for profiler passes; c5b is the fp32 R = 16 / 32 workload at
-112 MiB per rank).
+``--only {sweep, prefill, copy, c5, c5b, hier, ll_variants, ceilings}`` runs
+one part alone (for profiler passes; c5b is the fp32 R = 16 / 32 workload at
+112 MiB per rank, hier the same in the two-level order, fused and staged).
 """
 from __future__ import annotations
 
@@ -93,7 +93,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--only", choices=["all", "sweep", "prefill", "copy", "c5", "c5b",
+    ap.add_argument("--only", choices=["all", "sweep", "prefill", "copy", "c5", "c5b", "hier",
                                        "ll_variants", "ceilings"],
                     default="all", help="run one part (for profiler passes and ablations)")
     ap.add_argument("--configs", action="store_true",
@@ -190,21 +190,24 @@ class Bench:
         return round(statistics.median(ts) * 1e3, 3)
 
     # -- timings ------------------------------------------------------------
-    def graph_passes(self, sv, rv, n, proto, passes=1):
+    def graph_passes(self, sv, rv, n, proto, passes=1, call=None):
         """µs per call: 10 calls per graph, warmup replays, then ``passes``
-        timed passes of steps replays, each inside its own event pair."""
+        timed passes of steps replays, each inside its own event pair.
+        ``call`` (optional) makes one call on the current stream instead of
+        arAllReduce with the communicator."""
         torch = self.torch
+        one = call if call is not None else (lambda: self.launch(sv, rv, n, proto))
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             for _ in range(2):
-                self.launch(sv, rv, n, proto)
+                one()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(CALLS_PER_GRAPH):
-                self.launch(sv, rv, n, proto)
+                one()
         for _ in range(self.args.warmup):
             g.replay()
         torch.cuda.synchronize()
@@ -256,11 +259,12 @@ class Bench:
                 t.copy_(y)
         return fn
 
-    def back_to_back_us(self, sv, rv, n, proto, reps):
+    def back_to_back_us(self, sv, rv, n, proto, reps, call=None):
+        one = call if call is not None else (lambda: self.launch(sv, rv, n, proto))
         t0, t1 = self.events()
         t0.record()
         for _ in range(reps):
-            self.launch(sv, rv, n, proto)
+            one()
         t1.record()
         self.torch.cuda.synchronize()
         return t0.elapsed_time(t1) * 1000.0 / reps
@@ -480,6 +484,10 @@ def main():
                     B.comm.tune(torch.float16, R5, 1 << 19)
                 B.comm.tune(torch.float32, R5, C5B_BYTES)
         result["c5"] = run_c5(B, inputs, fp16=args.only != "c5b")
+
+    # ---- two-level order at the fp32 C5b shapes alone (for profiler passes) --
+    if args.only == "hier":
+        result["hier"] = run_hier(B, inputs, ((16, "fp32"), (32, "fp32")))
 
     # ---- HBM ceilings of the HB access pattern, beside HB itself -------------
     if args.only in ("all", "ceilings"):
@@ -705,6 +713,99 @@ def run_c5(B, inputs, fp16=True):
     return rows
 
 
+def run_hier(B, inputs, cases):
+    """The two-level order in nodes of 8 ranks at the C5 shapes: the flat fused
+    kernel, the fused kernel folding the two-level order in registers, the
+    staged two-level form (node partials in a workspace, a kernel boundary,
+    the fold across nodes), the same form through arAllReduceNoAlloc where its
+    partials fit the library's 64 MiB static scratch, and LL in nodes of 8 at
+    the fp16 size.  Each is checked against the grouped oracle (the flat one
+    against the oracle; fp32 on 2^20 sampled columns) and the exact integer
+    sums; graph-replayed at the fp16 size, back to back at the fp32 one."""
+    torch, ar = B.torch, B.ar
+    O = ar.arOption
+    rows = []
+    ws = None
+    for R, dtype in cases:
+        case = inputs.integer_case(R, dtype)
+        n = case["count"]
+        es = 4 if dtype == "fp32" else 2
+        x = inputs.make(**case)
+        exact = torch.zeros(n, dtype=torch.int32)
+        for r in range(R):
+            exact += x[r].to(torch.int32)
+        exact = exact.to(x.dtype).to(B.dev)
+        sv, rv = B.planes(x)
+        small = n <= (1 << 18)
+        sample = None if small else torch.randint(
+            0, n, (1 << 20,), generator=torch.Generator().manual_seed(98))
+        want = want_flat = None
+        if not B.args.no_parity:
+            xs = B.oracle_in(x if sample is None else x[:, sample].contiguous())
+            cast = (lambda a: a.view(B.np.uint32)) if dtype == "fp32" else \
+                (lambda a: a.view(B.np.uint16))
+            want = cast(B.orc.allreduce_grouped(xs, dtype, 8, nthreads=B.threads))
+            want_flat = cast(B.orc.allreduce(xs, dtype, nthreads=B.threads))
+        del x
+        need = (R // 8) * ((n * 4 + 255) // 256 * 256)
+        if ws is None or ws.numel() < need:
+            ws = None
+            ws = torch.empty(need, dtype=torch.uint8, device=B.dev)
+        B.comm.set_workspace(ws)
+        sp, rp = [t.data_ptr() for t in sv], [t.data_ptr() for t in rv]
+        code = ar.dtype_code(sv[0].dtype)
+
+        def no_alloc():
+            rc = ar.arAllReduceNoAlloc(sp, rp, n, code, ar.arRedOp.arSum, R, 8,
+                                       torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise ar.ArError(rc, "arAllReduceNoAlloc")
+        forms = [("hb", "flat", {}, None), ("hb", "fused, nodes of 8", {O.arOptNodeRanks: 8}, None),
+                 ("hb", "staged two-level, nodes of 8",
+                  {O.arOptNodeRanks: 8, O.arOptHBStaged: 1}, None)]
+        if need <= ar.AR_NOALLOC_SCRATCH_BYTES:
+            forms.append(("hb", "no-alloc two-level, nodes of 8", {}, no_alloc))
+        if small:
+            forms.append(("ll", "LL, nodes of 8", {O.arOptNodeRanks: 8}, None))
+        for proto, form, opts, call in forms:
+            for o, v in opts.items():
+                B.comm.set_option(o, v)
+            try:
+                for t in rv:
+                    t.view(torch.int16 if es == 2 else torch.int32).fill_(-23131)
+                (call or (lambda: B.launch(sv, rv, n, proto)))()
+                torch.cuda.synchronize()
+                rec = B.comm.last_launch() if call is None else None
+                par = None
+                if want is not None:
+                    got = B.np.stack([B.bits(t if sample is None else t[sample.to(t.device)])
+                                      for t in rv])
+                    par = bool(B.np.array_equal(got, want_flat if form == "flat" else want))
+                ex = all(torch.equal(rv[r], rv[0]) for r in range(1, R)) and \
+                    torch.equal(rv[0], exact)
+                if small:
+                    us = B.graph_passes(sv, rv, n, proto, call=call)[0]
+                    mode = "graph"
+                else:
+                    for _ in range(B.args.warmup):
+                        (call or (lambda: B.launch(sv, rv, n, proto)))()
+                    us = B.back_to_back_us(sv, rv, n, proto, B.args.steps, call=call)
+                    mode = "back-to-back"
+            finally:
+                for o in opts:
+                    B.comm.set_option(o, 0)
+            g = gbps(R, n, es, us)
+            rows.append({"R": R, "dtype": dtype, "elems_per_rank": n, "proto": proto,
+                         "form": form, "mode": mode, "us": round(us, 3), "gbps": g,
+                         "pct_of_peak": round(100 * g / HBM_PEAK_GBPS, 2), "parity": par,
+                         "exact_integer_sums": ex,
+                         "kernels": rec["kernels"] if rec else 2})
+            log(f"{dtype} R={R} {form}: {us:.2f} us, {g:.0f} GB/s, parity {par}, exact {ex}")
+        B.comm.set_workspace(None)
+        del sv, rv, exact
+    return rows
+
+
 def run_configs(B, inputs, sweep_rows, result):
     """Rows for every named workload (see the module docstring)."""
     torch = B.torch
@@ -785,44 +886,14 @@ def run_configs(B, inputs, sweep_rows, result):
             row["us"], None if row["parity"] is None else
             (row["parity"] and row["exact_integer_sums"]), o1, oT)
 
-    # NEXT-2: the hierarchical order (nodes of 8 ranks) at the C5 shapes, with
-    # each protocol that can run the size
-    O = B.ar.arOption
-    for R, dtype in ((16, "fp16"), (32, "fp16"), (32, "fp32")):
-        case = inputs.integer_case(R, dtype)
-        x = inputs.make(**case)
-        n = case["count"]
-        sv, rv = B.planes(x)
-        small = n <= (1 << 18)
-        sample = None if small else torch.randint(
-            0, n, (1 << 20,), generator=torch.Generator().manual_seed(98))
-        want = None
-        if not B.args.no_parity:
-            xs = x if sample is None else x[:, sample].contiguous()
-            want = B.orc.allreduce_grouped(B.oracle_in(xs), dtype, 8, nthreads=T)
-            want = want.view(B.np.uint32) if dtype == "fp32" else want.view(B.np.uint16)
-        for proto in (("hb", "ll") if small else ("hb",)):
-            B.comm.set_option(O.arOptNodeRanks, 8)
-            try:
-                B.launch(sv, rv, n, proto)
-                torch.cuda.synchronize()
-                par = None
-                if want is not None:
-                    got = B.np.stack([B.bits(t if sample is None else t[sample.to(t.device)])
-                                      for t in rv])
-                    par = bool(B.np.array_equal(got, want))
-                if small:
-                    us = B.graph_us(sv, rv, n, proto)
-                    mode = "graph, nodes of 8"
-                else:
-                    us = B.back_to_back_us(sv, rv, n, proto, B.args.steps)
-                    mode = "back-to-back, nodes of 8"
-            finally:
-                B.comm.set_option(O.arOptNodeRanks, 0)
-            add(f"C5{'a' if dtype == 'fp16' else 'b'} R={R} hierarchical", R, dtype, n, proto,
-                mode, us, par)
-        del x, sv, rv
-        log(f"hierarchical R={R} {dtype} done")
+    # NEXT-2: the two-level order (nodes of 8 ranks) at the C5 shapes: the
+    # fused kernel folding it in registers, the staged two-level form, the
+    # no-alloc entry point where its partials fit, LL at the fp16 size
+    for row in run_hier(B, inputs, ((16, "fp16"), (32, "fp16"), (16, "fp32"), (32, "fp32"))):
+        name = f"{'C5a' if row['dtype'] == 'fp16' else 'C5b'} R={row['R']} {row['form']}"
+        add(name, row["R"], row["dtype"], row["elems_per_rank"], row["proto"], row["mode"],
+            row["us"], None if row["parity"] is None else
+            (row["parity"] and row["exact_integer_sums"]))
 
     # HB5 ablation: the staged two-shot (reduce-scatter into the owner, kernel
     # boundary, all-gather from the owner) beside the fused rows above

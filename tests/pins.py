@@ -11,6 +11,9 @@ IEEE-754 definitions and from mathematics):
 * brute force   -- ``exact_model`` (exact rationals + an explicit RNE routine)
                    over every 3-rank column of a hand-picked value set, and
                    random columns at R = 8, 16, 32;
+* wide brute    -- ``exact_vec`` (an integer IEEE binary32 adder, itself
+                   checked against ``exact_model``) over 10^6 columns at
+                   R = 8, 16, 32 in five value regimes, flat and grouped;
 * hand cases    -- ``tests/golden/hand_cases.txt``, derived by hand;
 * closed form   -- integer-valued inputs sum exactly;
 * textbook case -- when every partial sum is exact, the result is the
@@ -115,6 +118,7 @@ def assert_same_bits(got: np.ndarray, want: np.ndarray, dtype: str, what: str):
 # brute force against the exact model
 # ---------------------------------------------------------------------------
 @functools.lru_cache(maxsize=None)
+@functools.lru_cache(maxsize=None)
 def _exhaustive_cols(dtype: str, R: int):
     vals = VALUE_SETS[dtype]
     cols = [list(c) for c in itertools.product(vals, repeat=R)]
@@ -158,6 +162,73 @@ def pin_bruteforce_random(orc, dtype: str, R: int, ncols: int, seed: int = 1):
     out = orc.allreduce(x, dtype, nthreads=2)
     for r in range(R):
         assert_same_bits(out[r], want, dtype, f"random {dtype} R={R} rank {r}")
+
+
+def mixed_bits(rng: np.random.Generator, dtype: str, ncols: int, R: int) -> np.ndarray:
+    """Finite columns (ncols, R) in five regimes, a fifth each: exponents in
+    [-12, 12]; exponent fields uniform below a per-column cap that is itself
+    uniform over the finite range (subnormal inputs and sums, and overflow of
+    the accumulator for bfloat16); exponents in [-1, 1] with random signs
+    (heavy cancellation, exact zeros); the first regime with a third of the
+    entries replaced by signed zeros; and only signed zeros, nine in ten
+    negative (so that all-negative-zero columns, whose sum is -0, occur)."""
+    fmt = em.FORMATS[dtype]
+    top = (1 << fmt.ebits) - 2
+    s = rng.integers(0, 2, (ncols, R), dtype=np.int64)
+    m = rng.integers(0, 1 << fmt.mbits, (ncols, R), dtype=np.int64)
+    regime = rng.integers(0, 5, (ncols, 1))
+    s = np.where(regime == 4, (rng.random((ncols, R)) < 0.9).astype(np.int64), s)
+    cap = rng.integers(0, top + 1, (ncols, 1))     # full range: a per-column top exponent
+    e = np.where(regime == 1, rng.integers(0, cap + 1, (ncols, R)),
+                 np.where(regime == 2, rng.integers(-1, 2, (ncols, R)) + fmt.bias,
+                          rng.integers(-12, 13, (ncols, R)) + fmt.bias))
+    bits = (s << (fmt.ebits + fmt.mbits)) | (e << fmt.mbits) | m
+    zero = ((regime == 3) & (rng.random((ncols, R)) < 1 / 3)) | (regime == 4)
+    bits = np.where(zero, s << (fmt.ebits + fmt.mbits), bits)
+    return bits.astype(np.uint32 if dtype == "fp32" else np.uint16)
+
+
+def pin_vector_model(dtype: str, seed: int = 21):
+    """``exact_vec`` (integer IEEE adder, used for the wide pin below) against
+    ``exact_model`` (exact rationals): every finite 3-rank column of the value
+    set, then mixed-regime random columns in the flat and grouped orders."""
+    import exact_vec as ev
+    fin = [v for v in VALUE_SETS[dtype] if not em.is_nan_bits(v, dtype)
+           and em.decode(v, em.FORMATS[dtype])[0] == "fin"]
+    cols, want = _exhaustive_cols(dtype, 3)
+    keep = np.array([all(v in fin for v in c) for c in cols])
+    got = ev.allreduce_columns(np.array(cols, dtype=np.int64)[keep], dtype)
+    assert np.array_equal(got, want[keep]), f"vector model, exhaustive {dtype}"
+    rng = np.random.default_rng(seed)
+    for R, ncols, group in ((2, 3000, None), (3, 2000, None), (8, 1000, None), (32, 300, None),
+                            (16, 400, 8), (8, 600, 2)):
+        bits = mixed_bits(rng, dtype, ncols, R)
+        got = ev.allreduce_columns(bits, dtype, group)
+        if group is None:
+            want = [em.allreduce_column([int(b) for b in row], dtype) for row in bits]
+        else:
+            want = [em.allreduce_column_grouped([int(b) for b in row], dtype, group)
+                    for row in bits]
+        bad = np.flatnonzero(got != np.array(want, dtype=np.int64))
+        assert bad.size == 0, (f"vector model {dtype} R={R} group={group}: "
+                               f"{[hex(int(b)) for b in bits[bad[0]]]}")
+
+
+def pin_bruteforce_wide(orc, dtype: str, R: int, ncols: int = 10**6, group: int | None = None,
+                        seed: int = 31):
+    """The oracle against ``exact_vec`` on ``ncols`` mixed-regime columns."""
+    import exact_vec as ev
+    bits = mixed_bits(np.random.default_rng(seed + R), dtype, ncols, R)
+    want = ev.allreduce_columns_chunked(bits, dtype, group)
+    x = bits.T.copy()
+    if dtype == "fp32":
+        x = x.view(np.float32)
+    if group is None:
+        out = orc.allreduce(x, dtype, nthreads=4)
+    else:
+        out = orc.allreduce_grouped(x, dtype, group, nthreads=4)
+    for r in range(R):
+        assert_same_bits(out[r], want, dtype, f"wide {dtype} R={R} group={group} rank {r}")
 
 
 # ---------------------------------------------------------------------------

@@ -39,6 +39,23 @@ def test_bruteforce_random(orc, dtype, R, ncols):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+def test_vector_model_agrees_with_exact_model(dtype):
+    pins.pin_vector_model(dtype)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("R", [8, 16, 32])
+def test_bruteforce_million_columns(orc, dtype, R):
+    pins.pin_bruteforce_wide(orc, dtype, R)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("R,group", [(16, 8), (32, 8)])
+def test_grouped_bruteforce_wide(orc, dtype, R, group):
+    pins.pin_bruteforce_wide(orc, dtype, R, ncols=200_000, group=group)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("R", [2, 3, 8, 16, 32])
 def test_integer_closed_form(orc, dtype, R):
     pins.pin_integer_closed_form(orc, dtype, R)
