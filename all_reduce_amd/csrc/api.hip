@@ -812,8 +812,8 @@ arResult_t arAllReduceNoAlloc(const void *const *sendbufs, void *const *recvbufs
     r = noalloc_device(dev, &d);
     if (r != arSuccess)
         return r;
-    // The HB defaults: 256 threads, one workgroup per CU, non-temporal
-    // accesses, interleaved chunks; no launch record.
+    // Each kernel's default launch shape (as arAllReduce with no shape
+    // options), non-temporal accesses, interleaved chunks; no launch record.
     const ar::HBConfig cfg = {d.cu_count, 1, true, nullptr};
     const int dtype = raw(dtype_arg);
     const hipError_t e =

