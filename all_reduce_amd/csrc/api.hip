@@ -582,6 +582,8 @@ arResult_t arAllReduce(const void *const *sendbufs, void *const *recvbufs, size_
     const bool two_level = group != 0 && proto == arProtoHB && staged;
     if (two_level) {
         const uint64_t need = ar::hier_workspace_bytes(count, nranks / group);
+        if (need == UINT64_MAX)
+            return reject(arInvalidArgument, "message too large for the two-level form");
         if (comm->ws == nullptr || comm->ws_bytes < need)
             return reject(arInvalidUsage, "the staged two-level form needs a workspace of "
                                           "(nranks / arOptNodeRanks) * roundup(count * 4, 256) "

@@ -231,11 +231,18 @@ hipError_t launch_hb_hier(const void *const *send, void *const *recv, size_t cou
                           uint64_t blocks, bool nt, hipStream_t stream);
 // Bytes between two nodes' partials, and the workspace the two-level form
 // needs: one binary32 per element per node, each node's share rounded up to
-// 256 bytes.
+// 256 bytes.  The workspace size saturates at UINT64_MAX instead of wrapping
+// (no message that passes argument validation comes near it), so a size
+// check against it can only refuse.
 inline uint64_t hier_partial_stride(uint64_t count) { return (count * 4 + 255) / 256 * 256; }
 inline uint64_t hier_workspace_bytes(uint64_t count, int nodes)
 {
-    return hier_partial_stride(count) * (uint64_t)nodes;
+    if (nodes <= 0)
+        return 0;
+    if (count > (UINT64_MAX - 255) / 4)
+        return UINT64_MAX;
+    const uint64_t stride = hier_partial_stride(count);
+    return stride > UINT64_MAX / (uint64_t)nodes ? UINT64_MAX : stride * (uint64_t)nodes;
 }
 // The LL one-shot with three-element packets (bfloat16 / float16 only, flat
 // order, cleared scheme, 8-byte packets).
