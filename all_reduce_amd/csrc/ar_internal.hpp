@@ -38,7 +38,7 @@ inline LLShape ll_default_shape(int nranks, uint64_t bytes_per_rank)
         {{256, 1}, {256, 2}, {256, 4}, {256, 8}, {256, 16}, {256, 64},
          {256, 64}, {256, 32}, {512, 32}, {512, 32}},
         {{512, 1}, {512, 1}, {512, 2}, {512, 4}, {256, 8}, {256, 32},
-         {256, 32}, {128, 128}, {512, 16}, {512, 16}},
+         {256, 64}, {128, 128}, {512, 16}, {512, 16}},
         {{512, 1}, {512, 1}, {512, 1}, {512, 2}, {512, 4}, {512, 16},
          {256, 16}, {128, 32}, {512, 8}, {512, 8}},
     };
