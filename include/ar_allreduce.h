@@ -173,9 +173,11 @@ typedef enum {
      * 512-byte group of a rank's packets carries a 32-bit sequence number in a
      * table owned by the communicator; producers flag packets with the
      * group's next number and the group's reader advances it, so nothing is
-     * cleared.  An ablation: slower on MI355X at every LL size, since each
-     * producer reads the table before it can store.  Both give the same
-     * results and may be mixed from call to call.  With 1, the launch shape
+     * cleared.  An ablation: slower on MI355X at every LL size, since the
+     * producer and the consumer of each group read its table entry before
+     * they can store or poll (hardware counters show the two extra reads per
+     * group), while the clears it saves are stores no one waits for.  Both
+     * give the same results and may be mixed from call to call.  With 1, the launch shape
      * comes from the LL options or the defaults, never the tuned table. */
     arOptLLFlagScheme = 12,
     /* Test hook: the value arCommReset writes to every sequence-table entry
