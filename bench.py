@@ -440,6 +440,8 @@ def main():
         # inside one event pair.
         avg_us = B.back_to_back_us(sv, sv, n, "hb", args.steps)
         pre["us_per_launch"] = round(avg_us, 2)
+        # The same calls graph-replayed (10 per graph, timed like the sweep).
+        pre["us_graph"] = round(B.graph_us(sv, sv, n, "hb"), 2)
         pre["gbps"] = gbps(R, n, 2, avg_us)
         pre["gbps_cold"] = gbps(R, n, 2, mean_us)
         result["hb_prefill"] = pre
@@ -452,7 +454,8 @@ def main():
             "kernel": "hb_twoshot<Bf16, R=8>", "bytes_per_launch": b_alg,
             "us_per_launch": pre["us_per_launch"],
         }
-        log(f"prefill HB in place: {pre['us_per_launch']:.1f} us per launch, {pre['gbps']:.0f} GB/s "
+        log(f"prefill HB in place: {pre['us_per_launch']:.1f} us per launch "
+            f"({pre['us_graph']:.1f} graph-replayed), {pre['gbps']:.0f} GB/s "
             f"({100 * pre['gbps'] / HBM_PEAK_GBPS:.1f}% of 8 TB/s), parity {pre['parity']}")
         del plane, backup, sv
 
@@ -822,7 +825,7 @@ def run_configs(B, inputs, sweep_rows, result):
     def add(name, R, dtype, n, proto, mode, us, parity, o1=None, oT=None):
         es = 4 if dtype == "fp32" else 2
         g = gbps(R, n, es, us)
-        hbm = counted.get((name, proto)) if mode in ("back-to-back", "cold") else None
+        hbm = counted.get((name, proto)) if mode in ("back-to-back", "cold", "graph") else None
         rows.append({"config": name, "R": R, "dtype": dtype, "elems_per_rank": n,
                      "bytes_per_rank": n * es, "proto": proto, "mode": mode,
                      "us_per_call": round(us, 2), "gbps": g,
@@ -869,6 +872,8 @@ def run_configs(B, inputs, sweep_rows, result):
             p["us_per_launch"], p["parity"], p.get("oracle_ms_1"), p.get("oracle_ms_T"))
         add("C4 8192x8192 in place", 8, "bf16", p["elems_per_rank"], "hb", "cold",
             p["us_mean_cold"], p["parity"], p.get("oracle_ms_1"), p.get("oracle_ms_T"))
+        add("C4 8192x8192 in place", 8, "bf16", p["elems_per_rank"], "hb", "graph",
+            p["us_graph"], p["parity"], p.get("oracle_ms_1"), p.get("oracle_ms_T"))
     # C5a / C5b: the rows measured by run_c5 (both chunk layouts), with the
     # oracle timed on the same inputs
     oracle_times = {}

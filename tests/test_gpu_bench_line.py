@@ -71,6 +71,8 @@ def test_prefill_roofline():
     line = _run("--only", "prefill", "--steps", "3", "--warmup", "1", "--no-cpu")
     _contract(line, 3, 1)
     assert line["hb_prefill"]["parity"] is True
+    # the graph-replayed figure of the same in-place calls, beside the back-to-back one
+    assert 0.5 < line["hb_prefill"]["us_graph"] / line["hb_prefill"]["us_per_launch"] < 2
     roof = line["roofline"]
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert roof["bytes_per_launch"] == 2 << 30
