@@ -1,11 +1,18 @@
 /* A plain C99 caller of the all-reduce C ABI on the GPU: device memory from
  * the HIP runtime API, no Python and no torch.  R = 8 ranks of integer-valued
  * bf16 (exact sums), out of place and in place, each protocol and both LL flag
- * schemes; every output element is compared with the exact integer sum. */
+ * schemes; every output element is compared with the exact integer sum.
+ *
+ * With --time it then prints the host's cost of eager calls from C: the mean
+ * wall-clock time per call of 2000 back-to-back arAllReduce calls (after 200
+ * untimed ones), up to a final device synchronisation, for the smallest call
+ * (HB, one rank, 16 bytes) and for LL and HB at 8 ranks x 2 KiB. */
+#define _POSIX_C_SOURCE 199309L
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+#include <time.h>
 
 #include <hip/hip_runtime_api.h>
 
@@ -31,8 +38,37 @@ static int check_hip(hipError_t e, const char *what)
     return 0;
 }
 
-int main(void)
+static double now_us(void)
 {
+    struct timespec t;
+    clock_gettime(CLOCK_MONOTONIC, &t);
+    return t.tv_sec * 1e6 + t.tv_nsec * 1e-3;
+}
+
+/* Mean microseconds per eager call, or a negative value on an error. */
+static double eager_us(void *const *sendp, void *const *recvp, size_t count, int nranks,
+                       arProtocol_t proto, arComm_t comm)
+{
+    for (int i = 0; i < 200; ++i)
+        if (arAllReduce((const void *const *)sendp, recvp, count, arBfloat16, arSum, nranks, proto,
+                        comm, NULL) != arSuccess)
+            return -1.0;
+    if (hipDeviceSynchronize() != hipSuccess)
+        return -1.0;
+    const int calls = 2000;
+    const double t0 = now_us();
+    for (int i = 0; i < calls; ++i)
+        if (arAllReduce((const void *const *)sendp, recvp, count, arBfloat16, arSum, nranks, proto,
+                        comm, NULL) != arSuccess)
+            return -1.0;
+    if (hipDeviceSynchronize() != hipSuccess)
+        return -1.0;
+    return (now_us() - t0) / calls;
+}
+
+int main(int argc, char **argv)
+{
+    const int timing = argc > 1 && strcmp(argv[1], "--time") == 0;
     static uint16_t host[R][N], out[N], want[N];
     unsigned s = 12345u;
     for (int i = 0; i < N; ++i) {
@@ -89,6 +125,20 @@ int main(void)
                     ++failures;
                 }
             }
+        }
+    }
+    if (timing && failures == 0) {
+        if (arCommSetOption(comm, arOptLLFlagScheme, 0) != arSuccess)
+            ++failures;
+        const double floor_us = eager_us(sendp, recvp, 8, 1, arProtoHB, comm);
+        const double ll_us = eager_us(sendp, recvp, 1024, R, arProtoLL, comm);
+        const double hb_us = eager_us(sendp, recvp, 1024, R, arProtoHB, comm);
+        if (floor_us < 0 || ll_us < 0 || hb_us < 0) {
+            printf("FAIL: timed calls\n");
+            ++failures;
+        } else {
+            printf("eager us per call from C: hb_1rank_16B %.2f ll_8x2KiB %.2f hb_8x2KiB %.2f\n",
+                   floor_us, ll_us, hb_us);
         }
     }
     for (int r = 0; r < R; ++r) {
