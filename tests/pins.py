@@ -13,7 +13,8 @@ IEEE-754 definitions and from mathematics):
                    random columns at R = 8, 16, 32;
 * wide brute    -- ``exact_vec`` (an integer IEEE binary32 adder, itself
                    checked against ``exact_model``) over 10^6 columns at
-                   R = 8, 16, 32 in five value regimes, flat and grouped;
+                   R = 8, 16, 32 in five value regimes, flat, and grouped in
+                   nodes of 2, 4 and 8;
 * hand cases    -- ``tests/golden/hand_cases.txt``, derived by hand;
 * closed form   -- integer-valued inputs sum exactly;
 * textbook case -- when every partial sum is exact, the result is the

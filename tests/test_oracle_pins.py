@@ -50,7 +50,7 @@ def test_bruteforce_million_columns(orc, dtype, R):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("R,group", [(16, 8), (32, 8)])
+@pytest.mark.parametrize("R,group", [(16, 8), (32, 8), (32, 4), (8, 2)])
 def test_grouped_bruteforce_wide(orc, dtype, R, group):
     pins.pin_bruteforce_wide(orc, dtype, R, ncols=200_000, group=group)
 
