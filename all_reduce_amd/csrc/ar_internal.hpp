@@ -93,6 +93,28 @@ inline int hb_default_threads(int nranks, uint64_t bytes_per_rank)
     return 128;
 }
 
+// Default workgroups per CU of the fused HB kernel.  Each lane holds one
+// 16-byte vector per rank in flight, so with few ranks one workgroup per CU
+// leaves HBM idle: measured on MI355X (bf16, 4-128 MiB per rank, in place and
+// out of place), the fastest point keeps about 2048 loads in flight per CU
+// for 256-thread workgroups -- 8 workgroups per CU at 1 rank (44 against
+// 131 us at 128 MiB), 4 at 2, 3 at 3, 2 at 4 and 5, 1 from 6 -- and 4 (2 up
+// to 16 MiB per rank) for 9 to 15 ranks, whose default is 64 threads above
+// 16 MiB (12 ranks, 128 MiB: 587-620 against 1172 us).  Below 4 MiB per rank
+// and at 8, 16 and from 17 ranks, one.
+inline int hb_default_blocks_per_cu(int nranks, uint64_t bytes_per_rank)
+{
+    if (bytes_per_rank < ((uint64_t)4 << 20))
+        return 1;
+    if (nranks <= 5) {
+        static constexpr int kPerCU[6] = {1, 8, 4, 3, 2, 2};
+        return kPerCU[nranks < 0 ? 0 : nranks];
+    }
+    if (nranks >= 9 && nranks <= 15)
+        return bytes_per_rank > ((uint64_t)16 << 20) ? 4 : 2;
+    return 1;
+}
+
 // LL flag schemes (the values of arOptLLFlagScheme): the reader zeroes each
 // consumed packet (the default), or each 512-byte packet group carries a
 // sequence number.

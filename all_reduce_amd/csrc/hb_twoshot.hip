@@ -111,9 +111,22 @@ __global__ __launch_bounds__(hb_max_threads(RMAX)) void hb_twoshot(HBParams<RMAX
             const uint64_t i = base + (uint64_t)u * nthr + threadIdx.x;
             if (i < end) {
 #pragma unroll
-                for (int j = 0; j < RMAX; ++j)
-                    if (EXACT || j < (int)n)
+                for (int j = 0; j < RMAX; ++j) {
+                    if constexpr (EXACT) {
                         v[u][j] = load16<NT>((const u32x4 *)p.rk.send[j] + i);
+                    } else {
+                        // Generic rank table: every slot loads, so that the
+                        // loads issue back to back with no branch (and no
+                        // wait) between them.  A slot past the group rereads
+                        // this lane's own vector of rank 0 -- an address the
+                        // lane reads anyway and writes only after all its
+                        // loads -- and is never accumulated.
+                        const bool live = j < (int)n;
+                        const u32x4 *row = live ? (const u32x4 *)p.rk.send[j]
+                                                : (const u32x4 *)p.rk.send[0];
+                        v[u][j] = load16<NT>(row + i);
+                    }
+                }
             }
         }
 #pragma unroll
@@ -259,13 +272,17 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     int u = cfg.unroll > 0 ? cfg.unroll : 1;
     if (u > max_unroll(RMAX))
         u = max_unroll(RMAX);
-    // Default: one workgroup per CU -- measured on MI355X, fewer loads in
-    // flight per CU stream HBM faster -- of hb_default_threads threads.
+    // Defaults: hb_default_threads threads and hb_default_blocks_per_cu
+    // workgroups per CU (one for 6 to 8 and from 16 ranks: there, fewer loads
+    // in flight per CU stream HBM faster; more for fewer ranks).
     uint32_t threads = want_threads > 0 ? (uint32_t)want_threads
                                         : (uint32_t)hb_default_threads(nranks, count * T::kBytes);
     if (threads > (uint32_t)hb_max_threads(RMAX))
         threads = (uint32_t)hb_max_threads(RMAX);
-    const uint64_t blocks = want_blocks > 0 ? want_blocks : (uint64_t)cfg.cu_count;
+    const uint64_t blocks =
+        want_blocks > 0 ? want_blocks
+                        : (uint64_t)cfg.cu_count *
+                              (uint64_t)hb_default_blocks_per_cu(nranks, count * T::kBytes);
 
     // Enough workgroups to fill the chip, but never more per chunk than the
     // largest chunk has tiles.
@@ -274,7 +291,12 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
                                  ? (p.nvec + (uint64_t)nranks - 1) / (uint64_t)nranks
                                  : p.nvec - p.chunk_vec * (uint64_t)(nranks - 1);
     const uint64_t tiles = (largest + tile - 1) / tile;
-    const uint64_t want = (blocks + (uint64_t)nranks - 1) / (uint64_t)nranks;
+    // Workgroups per chunk rounded down: a grid just above a multiple of the
+    // CU count would leave a few CUs with twice the work (R = 3 at one per
+    // CU: 86 x 3 = 258 workgroups on 256 CUs).
+    uint64_t want = blocks / (uint64_t)nranks;
+    if (want < 1)
+        want = 1;
     uint64_t bpc = tiles < want ? tiles : want;
     if (bpc < 1)
         bpc = 1;

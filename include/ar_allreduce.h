@@ -90,8 +90,12 @@ typedef enum {
      * rank count and message size (a table measured on MI355X; with only
      * arOptLLThreads set, as many lanes per rank as the default has). */
     arOptLLBlocksPerRank = 1,
-    /* HB: workgroups in the grid (rounded to a multiple of nranks, capped by
-     * the message's tiles); 0 = one per compute unit. */
+    /* HB: workgroups in the grid (rounded down to a multiple of nranks, at
+     * least nranks, capped by the message's tiles); 0 = the built-in default:
+     * one per compute unit, more from 4 MiB per rank for fewer than 6 ranks
+     * (8 per CU at 1 rank down to 2 at 4 and 5) and for 9 to 15 ranks (2, or 4
+     * above 16 MiB), where one per CU keeps too few loads in flight (measured
+     * on MI355X). */
     arOptHBBlocks = 2,
     /* HB: 1 = non-temporal loads and stores, 0 = ordinary (cached) ones.
      * -1 (default): the policy the tuner chose for the message size and mode,

@@ -210,9 +210,10 @@ def test_last_launch_record(orc):
         run_allreduce(c, y, "hb")
         rec = c.last_launch()
         assert rec["protocol"] == ar.arProtocol.arProtoHB and rec["nonTemporal"] == 1
-        # one workgroup per CU, rounded up to whole chunks, at most the 32
+        # one workgroup per CU, rounded down to whole chunks, at most the 32
         # tiles of 256 vectors that each of the 8 interleaved chunks has
-        assert (rec["grid"], rec["threads"], rec["staged"]) == (min(-(-cus // 8), 32) * 8, 256, 0)
+        assert (rec["grid"], rec["threads"], rec["staged"]) == (
+            min(max(cus // 8, 1), 32) * 8, 256, 0)
         c.set_option(ar.arOption.arOptHBStaged, 1)
         run_allreduce(c, y, "hb")
         assert c.last_launch()["kernels"] == 2 and c.last_launch()["staged"] == 1
