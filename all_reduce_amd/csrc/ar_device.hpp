@@ -100,4 +100,47 @@ struct RankTable {
     void *recv[R];
 };
 
+// The same table held by a wave, one entry per lane: lane r < R holds send[r],
+// lane 32 + r holds recv[r].  A pointer is read back with two lane reads where
+// it is used, so that the table never sits in scalar registers whole: 32
+// ranks' 64 pointers need 128 of them, more than a wave has, and the compiler
+// then spills and reloads them in blocks around every use.  The pointers come
+// back through a global-memory pointer so that accesses stay global ones
+// (a pointer rebuilt from integers would otherwise be a flat one).
+template <int R>
+struct WaveTable {
+    static_assert(R <= 32, "one wave holds at most 32 send and 32 recv pointers");
+    uint64_t v = 0;
+    WaveTable() = default;
+    __device__ explicit WaveTable(const RankTable<R> &t)
+    {
+        const uint32_t lane = __lane_id();
+        const uint32_t r = lane & 31u;
+        uint64_t e = 0;
+        if (r < (uint32_t)R)
+            e = lane < 32u ? (uint64_t)t.send[r] : (uint64_t)t.recv[r];
+        v = e;
+        // The load completes here, not at the top of a loop that uses it,
+        // where the wait would also take in the loop's own stores.
+        asm volatile("" : "+v"(v));
+    }
+    // Called at the top of a loop: keeps the compiler from hoisting the lane
+    // reads out of it, which would bring back the scalar-register table.
+    __device__ void refresh() { asm volatile("" : "+v"(v)); }
+    __device__ uint64_t get(int lane) const
+    {
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane);
+        return ((uint64_t)hi << 32) | lo;
+    }
+    __device__ const void *send(int r) const
+    {
+        return (const void *)(const __attribute__((address_space(1))) char *)get(r);
+    }
+    __device__ void *recv(int r) const
+    {
+        return (void *)(__attribute__((address_space(1))) char *)get(32 + r);
+    }
+};
+
 }  // namespace ar

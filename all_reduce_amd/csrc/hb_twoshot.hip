@@ -195,11 +195,145 @@ __global__ __launch_bounds__(hb_max_threads(RMAX)) void hb_twoshot(HBParams<RMAX
     }
 }
 
+// The kernel above for a 32-rank table at one vector per lane, reading the
+// table from a wave-held copy (WaveTable) instead of scalar registers, where
+// 64 pointers do not fit: the compiler spills them and reloads them in blocks.
+// Same chunks, same order of additions, same results.  On MI355X, bf16 and
+// fp16: 3.6 against 4.8 us at 2 KiB per rank, 6.1 against 7.1 us at 512 KiB,
+// 189 against 191 us at 16 MiB (24 ranks: 4.6 against 6.4 us at 2 KiB); at
+// 112 MiB per rank of fp32 the scalar table is 1-2 % faster, so the launch
+// takes this kernel up to kWaveTableMaxBytes per rank.  A separate kernel
+// rather than a switch in the one above, whose code stays as it is.
+template <typename T, bool EXACT, bool NT, int NODE>
+__global__ __launch_bounds__(hb_max_threads(32)) void hb_twoshot_wave(HBParams<32> p)
+{
+    constexpr int RMAX = 32;
+    constexpr bool kGrouped = NODE != 0;
+    const uint32_t n = EXACT ? RMAX : p.nranks;
+    const uint32_t node = NODE > 0 ? (uint32_t)NODE : p.group;
+    const uint32_t nthr = blockDim.x;
+    const uint32_t c = blockIdx.x % n;
+    const uint32_t bb = blockIdx.x / n;
+    uint64_t start, step, end;
+    if (p.interleaved) {
+        start = ((uint64_t)bb * n + c) * nthr;
+        step = (uint64_t)p.blocks_per_chunk * n * nthr;
+        end = p.nvec;
+    } else {
+        const uint64_t c0 = (uint64_t)c * p.chunk_vec;
+        start = c0 + (uint64_t)bb * nthr;
+        step = (uint64_t)p.blocks_per_chunk * nthr;
+        end = (c == n - 1) ? p.nvec : c0 + p.chunk_vec;
+    }
+
+    constexpr int U = 1;
+    WaveTable<RMAX> wt(p.rk);
+    for (uint64_t base = start; base < end; base += step) {
+        // The table, the run-time rank count and the node size are re-read
+        // each tile: hoisted out of the loop, the lane reads and the per-rank
+        // tests would hold scalar registers across it again.
+        wt.refresh();
+        uint32_t nl = n, ndl = node;
+        if constexpr (!EXACT)
+            asm volatile("" : "+s"(nl));
+        if constexpr (NODE < 0)
+            asm volatile("" : "+s"(ndl));
+        // The loop has hb_twoshot's shape, vector loop included: written more
+        // compactly, the compiler interleaved the sums with the loads and
+        // fewer loads were in flight (5 % slower at 16 MiB per rank).
+        u32x4 v[U][RMAX];
+        // reduce-scatter: every load of the tile is issued before any use (a
+        // slot past a generic table's count rereads rank 0's vector and is
+        // not added)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t i = base + (uint64_t)u * nthr + threadIdx.x;
+            if (i < end) {
+#pragma unroll
+                for (int j = 0; j < RMAX; ++j)
+                    v[u][j] = load16<NT>((const u32x4 *)wt.send(EXACT || j < (int)nl ? j : 0) + i);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t i = base + (uint64_t)u * nthr + threadIdx.x;
+            if (i < end) {
+                u32x4 y;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float acc[T::kPerWord];
+                    float total[T::kPerWord] = {};
+                    T::widen(v[u][0][q], acc);
+#pragma unroll
+                    for (int j = 1; j < RMAX; ++j) {
+                        if (EXACT || j < (int)nl) {
+                            float x[T::kPerWord];
+                            T::widen(v[u][j][q], x);
+                            if (kGrouped && (uint32_t)j % ndl == 0) {
+#pragma unroll
+                                for (int e = 0; e < T::kPerWord; ++e) {
+                                    total[e] = (uint32_t)j == ndl ? acc[e] : total[e] + acc[e];
+                                    acc[e] = x[e];
+                                }
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < T::kPerWord; ++e)
+                                    acc[e] = acc[e] + x[e];
+                            }
+                        }
+                    }
+                    if (kGrouped) {
+#pragma unroll
+                        for (int e = 0; e < T::kPerWord; ++e)
+                            acc[e] = total[e] + acc[e];
+                    }
+                    y[q] = T::narrow(acc);
+                }
+                // all-gather
+#pragma unroll
+                for (int r = 0; r < RMAX; ++r)
+                    if (EXACT || r < (int)nl)
+                        store16<NT>((u32x4 *)wt.recv(r) + i, y);
+            }
+        }
+    }
+
+    if (p.tail_elems != 0 && blockIdx.x == gridDim.x - 1 && threadIdx.x < p.tail_elems) {
+        constexpr uint64_t kPerVec = 16 / T::kBytes;
+        const uint64_t i = p.nvec * kPerVec + threadIdx.x;
+        float a = load_elem<T>(p.rk.send[0], i);
+        float total = 0.0f;
+        for (uint32_t j = 1; j < n; ++j) {
+            const float x = load_elem<T>(p.rk.send[j], i);
+            if (kGrouped && j % node == 0) {
+                total = j == node ? a : total + a;
+                a = x;
+            } else {
+                a = a + x;
+            }
+        }
+        if (kGrouped)
+            a = total + a;
+        for (uint32_t r = 0; r < n; ++r)
+            store_elem<T>(p.rk.recv[r], i, a);
+    }
+}
+
+// Largest message per rank that takes hb_twoshot_wave.
+constexpr uint64_t kWaveTableMaxBytes = (uint64_t)16 << 20;
+
 namespace {
 
 template <typename T, int RMAX, bool EXACT, int U, bool NT, int NODE = 0>
 hipError_t launch_one(const HBParams<RMAX> &p, uint32_t grid, uint32_t threads, hipStream_t stream)
 {
+    if constexpr (RMAX == 32 && U == 1) {
+        if (p.nvec * 16 <= kWaveTableMaxBytes) {
+            hipLaunchKernelGGL((hb_twoshot_wave<T, EXACT, NT, NODE>), dim3(grid), dim3(threads), 0,
+                               stream, p);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((hb_twoshot<T, RMAX, EXACT, U, NT, NODE>), dim3(grid), dim3(threads), 0,
                        stream, p);
     return hipGetLastError();

@@ -253,6 +253,50 @@ def test_tails_and_rank_counts(comm, orc, dtype, R, N, protocol):
     check(comm, orc, x, protocol)
 
 
+@pytest.mark.parametrize("R", [6, 7, 9, 15, 17, 31])
+@pytest.mark.parametrize("kib", [2, 256, 1024])
+def test_generic_rank_tables(comm, orc, R, kib):
+    """A rank count without a kernel of its own runs the next larger table (4,
+    8, 16 or 32 slots) with the count at run time: LL and HB at the edges of
+    each table, LL's word-packet and three-element-packet sizes, one element
+    short of a power of two (a partial last packet and vector)."""
+    N = kib * 512 - 1
+    x = inputs.make(R, N, "bf16", "normal", seed=6000 + R * 13 + kib)
+    for protocol in ("ll", "hb"):
+        check(comm, orc, x, protocol, what=f"{protocol} generic table R={R} {kib} KiB")
+
+
+@functools.lru_cache(maxsize=2)
+def _wave_bound_case(R, extra):
+    N = (16 << 20) // 2 + extra
+    x = inputs.make(R, N, "bf16", "int4", seed=7000 + R + extra)
+    exact = torch.zeros(N, dtype=torch.int32)
+    for r in range(R):
+        exact += x[r].to(torch.int32)
+    return x, exact
+
+
+@pytest.mark.parametrize("inplace", [False, True], ids=["out", "inplace"])
+@pytest.mark.parametrize("extra", [0, 8], ids=["at_bound", "one_vector_over"])
+@pytest.mark.parametrize("R", [24, 32])
+def test_hb_wave_table_size_bound(comm, orc, R, extra, inplace):
+    """32-slot tables (32 ranks, and 24 on the generic table) run the HB kernel
+    that reads the rank table from a wave-held copy up to 16 MiB per rank and
+    the scalar-table kernel above: bf16 integers at exactly 16 MiB per rank and
+    one 16-byte vector more, exact sums on every element of every rank, the
+    oracle on sampled columns."""
+    x, exact = _wave_bound_case(R, extra)
+    note(f"hb wave-table bound R={R} extra={extra} inplace={inplace}")
+    got = run_allreduce(comm, x, "hb", inplace=inplace)
+    exact_b = exact.to(torch.bfloat16)
+    for r in range(R):
+        assert torch.equal(got[r], exact_b), f"rank {r}"
+    g = torch.Generator().manual_seed(98)
+    idx = torch.randint(0, x.shape[1], (1 << 16,), generator=g)
+    idx[0] = x.shape[1] - 1
+    assert_parity(got[:, idx].contiguous(), expect(orc, x[:, idx].contiguous()),
+                  f"hb wave-table bound R={R} extra={extra} inplace={inplace} sampled")
+
 @pytest.mark.parametrize("nt", [0, 1])
 @pytest.mark.parametrize("unroll", [1, 2, 4])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
