@@ -157,12 +157,18 @@ __global__ __launch_bounds__(kHierMaxThreads) void hb_hier_fold(HierParams p)
     const uint32_t G = GC > 0 ? (uint32_t)GC : p.nodes;
     const uint32_t n = p.nranks;
     const uint64_t nthr = blockDim.x;
+    WaveTable<AR_MAX_RANKS> wt(p.rk);
     for (uint64_t i = (uint64_t)blockIdx.x * nthr + threadIdx.x; i < p.nvec;
          i += (uint64_t)gridDim.x * nthr) {
+        wt.refresh();
+        uint32_t nl = n, Gl = G;
+        asm volatile("" : "+s"(nl));
+        if constexpr (GC == 0)
+            asm volatile("" : "+s"(Gl));
         u32x4 pv[GMAX][H];
 #pragma unroll
         for (int g = 0; g < GMAX; ++g)
-            if (GC > 0 || g < (int)G)
+            if (GC > 0 || g < (int)Gl)
 #pragma unroll
                 for (int h = 0; h < H; ++h)
                     pv[g][h] = load16<NT>((const u32x4 *)(p.ws + g * p.pstride + i * PV) + h);
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(kHierMaxThreads) void hb_hier_fold(HierParams p)
             total[e] = as_float(pv[0][e / 4][e % 4]);
 #pragma unroll
         for (int g = 1; g < GMAX; ++g)
-            if (GC > 0 || g < (int)G)
+            if (GC > 0 || g < (int)Gl)
 #pragma unroll
                 for (int e = 0; e < PV; ++e)
                     total[e] = total[e] + as_float(pv[g][e / 4][e % 4]);
@@ -185,8 +191,8 @@ __global__ __launch_bounds__(kHierMaxThreads) void hb_hier_fold(HierParams p)
             y[q] = T::narrow(total + q * T::kPerWord);
 #pragma unroll
         for (int r = 0; r < AR_MAX_RANKS; ++r)
-            if (r < (int)n)
-                store16<NT>((u32x4 *)p.rk.recv[r] + i, y);
+            if (r < (int)nl)
+                store16<NT>((u32x4 *)wt.recv(r) + i, y);
     }
 
     if (p.tail_elems != 0 && blockIdx.x == gridDim.x - 1 && threadIdx.x < p.tail_elems) {
