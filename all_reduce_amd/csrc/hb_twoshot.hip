@@ -64,6 +64,16 @@ __device__ inline void store_elem(void *base, uint64_t i, float a)
         ((uint32_t *)base)[i] = w;
 }
 
+// A vector of -0 in the element type, loaded by a generic table's slots past
+// the rank count: adding -0 leaves every binary32 value as it is.
+__device__ u32x4 kNegZero16 = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+__device__ u32x4 kNegZero32 = {0x80000000u, 0x80000000u, 0x80000000u, 0x80000000u};
+template <typename T>
+__device__ inline const u32x4 *neg_zero_vec()
+{
+    return T::kBytes == 2 ? &kNegZero16 : &kNegZero32;
+}
+
 // Largest workgroup compiled for a rank-table size: the R 16-byte vectors a
 // lane holds (4 VGPRs each) must fit the register share of that many threads.
 constexpr int hb_max_threads(int rmax) { return rmax >= 32 ? 256 : (rmax >= 16 ? 512 : 1024); }
@@ -117,14 +127,27 @@ __global__ __launch_bounds__(hb_max_threads(RMAX)) void hb_twoshot(HBParams<RMAX
                     } else {
                         // Generic rank table: every slot loads, so that the
                         // loads issue back to back with no branch (and no
-                        // wait) between them.  A slot past the group rereads
-                        // this lane's own vector of rank 0 -- an address the
-                        // lane reads anyway and writes only after all its
-                        // loads -- and is never accumulated.
+                        // wait) between them.  In the flat order a slot past
+                        // the group loads a vector of -0 and is added like the
+                        // others: x + (-0) is x for every binary32 x (signed
+                        // zeros, subnormals, infinities; a NaN is already
+                        // quiet after the group's own additions), and the
+                        // sums need no per-rank branch (on MI355X 8-25 %
+                        // faster at 2 KiB-1 MiB per rank, 3 to 24 ranks).  In
+                        // the hierarchical order it rereads this lane's own
+                        // vector of rank 0 -- an address the lane reads
+                        // anyway and writes only after all its loads -- and
+                        // is never accumulated.
                         const bool live = j < (int)n;
-                        const u32x4 *row = live ? (const u32x4 *)p.rk.send[j]
-                                                : (const u32x4 *)p.rk.send[0];
-                        v[u][j] = load16<NT>(row + i);
+                        if constexpr (NODE == 0) {
+                            const u32x4 *at = live ? (const u32x4 *)p.rk.send[j] + i
+                                                   : neg_zero_vec<T>();
+                            v[u][j] = load16<NT>(at);
+                        } else {
+                            const u32x4 *row = live ? (const u32x4 *)p.rk.send[j]
+                                                    : (const u32x4 *)p.rk.send[0];
+                            v[u][j] = load16<NT>(row + i);
+                        }
                     }
                 }
             }
@@ -141,7 +164,7 @@ __global__ __launch_bounds__(hb_max_threads(RMAX)) void hb_twoshot(HBParams<RMAX
                     T::widen(v[u][0][q], acc);
 #pragma unroll
                     for (int j = 1; j < RMAX; ++j) {
-                        if (EXACT || j < (int)n) {
+                        if (EXACT || NODE == 0 || j < (int)n) {
                             float x[T::kPerWord];
                             T::widen(v[u][j][q], x);
                             if (kGrouped && (uint32_t)j % node == 0) {
@@ -242,16 +265,19 @@ __global__ __launch_bounds__(hb_max_threads(32)) void hb_twoshot_wave(HBParams<3
         // compactly, the compiler interleaved the sums with the loads and
         // fewer loads were in flight (5 % slower at 16 MiB per rank).
         u32x4 v[U][RMAX];
-        // reduce-scatter: every load of the tile is issued before any use (a
-        // slot past a generic table's count rereads rank 0's vector and is
-        // not added)
+        // reduce-scatter: every load of the tile is issued before any use
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint64_t i = base + (uint64_t)u * nthr + threadIdx.x;
             if (i < end) {
 #pragma unroll
                 for (int j = 0; j < RMAX; ++j)
-                    v[u][j] = load16<NT>((const u32x4 *)wt.send(EXACT || j < (int)nl ? j : 0) + i);
+                    // (slots past a generic table's count: as in hb_twoshot)
+                    if constexpr (!EXACT && NODE == 0)
+                        v[u][j] = load16<NT>(j < (int)nl ? (const u32x4 *)wt.send(j) + i
+                                                          : neg_zero_vec<T>());
+                    else
+                        v[u][j] = load16<NT>((const u32x4 *)wt.send(EXACT || j < (int)nl ? j : 0) + i);
             }
         }
 #pragma unroll
@@ -266,7 +292,7 @@ __global__ __launch_bounds__(hb_max_threads(32)) void hb_twoshot_wave(HBParams<3
                     T::widen(v[u][0][q], acc);
 #pragma unroll
                     for (int j = 1; j < RMAX; ++j) {
-                        if (EXACT || j < (int)nl) {
+                        if (EXACT || NODE == 0 || j < (int)nl) {
                             float x[T::kPerWord];
                             T::widen(v[u][j][q], x);
                             if (kGrouped && (uint32_t)j % ndl == 0) {

@@ -358,6 +358,27 @@ def test_exhaustive_value_set_three_ranks(comm, protocol, dtype):
         pins.assert_same_bits(bits(got[r]), want, dtype, f"value set {dtype} rank {r}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("R", [5, 7, 12, 24])
+@pytest.mark.parametrize("protocol", ["ll", "hb"])
+def test_generic_tables_special_values(comm, orc, protocol, R, dtype):
+    """Rank counts without a kernel of their own (the slots of the table past the
+    count load -0 and add it, an exact identity, in HB's flat order) over
+    signed zeros, all-negative-zero columns, subnormals, cancellation and
+    overflow, with one entry in a hundred an infinity or a NaN: bit-exact
+    against the oracle (NaNs by class)."""
+    rng = np.random.default_rng(700 + 13 * R)
+    cols = pins.mixed_bits(rng, dtype, 8192 + 5, R)
+    fmt = em.FORMATS[dtype]
+    sign = 1 << (fmt.ebits + fmt.mbits)
+    inf = ((1 << fmt.ebits) - 1) << fmt.mbits
+    qnan = inf | (1 << (fmt.mbits - 1)) | 1
+    kind = rng.integers(0, 3, cols.shape)
+    special = np.where(kind == 0, inf, np.where(kind == 1, inf | sign, qnan))
+    cols = np.where(rng.random(cols.shape) < 0.01, special, cols).astype(cols.dtype)
+    x = from_bits(np.ascontiguousarray(cols.T), dtype)
+    check(comm, orc, x, protocol, what=f"{protocol} generic table special values R={R} {dtype}")
+
 @pytest.mark.parametrize("protocol", ["ll", "hb"])
 def test_hand_cases(comm, protocol):
     for dtype, ins, out in pins.load_hand_cases():
