@@ -106,7 +106,9 @@ struct RankTable {
 // ranks' 64 pointers need 128 of them, more than a wave has, and the compiler
 // then spills and reloads them in blocks around every use.  The pointers come
 // back through a global-memory pointer so that accesses stay global ones
-// (a pointer rebuilt from integers would otherwise be a flat one).
+// (a pointer rebuilt from integers would otherwise be a flat one).  Every wave
+// must be whole (64 lanes): the kernels that use it are launched with
+// workgroups of a multiple of 64 threads, which the options check enforces.
 template <int R>
 struct WaveTable {
     static_assert(R <= 32, "one wave holds at most 32 send and 32 recv pointers");

@@ -36,22 +36,38 @@ struct StagedParams {
 
 constexpr int staged_max_threads(int rmax) { return rmax >= 32 ? 256 : (rmax >= 16 ? 512 : 1024); }
 
+// The generic 32-slot table (17 to 31 ranks) is read from a wave-held copy
+// (WaveTable), the run-time rank count re-read each tile, as in
+// hb_twoshot_wave: in scalar registers its pointers and per-rank tests spill
+// (48-74 lane writes per kernel).  The exact 32-rank kernels do not spill.
+constexpr bool staged_wave_table(int rmax, bool exact) { return rmax >= 32 && !exact; }
+
 template <typename T, int RMAX, bool EXACT, bool NT>
 __global__ __launch_bounds__(staged_max_threads(RMAX)) void hb_stage_reduce(StagedParams<RMAX> p)
 {
     const uint32_t n = EXACT ? RMAX : p.nranks;
     const uint64_t tile = blockDim.x;
     const uint64_t ntiles = (p.nvec + tile - 1) / tile;
+    constexpr bool kWT = staged_wave_table(RMAX, EXACT);
+    WaveTable<RMAX> wt;
+    if constexpr (kWT)
+        wt = WaveTable<RMAX>(p.rk);
     for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const uint32_t c = (uint32_t)(t % n);
+        uint32_t nl = n;
+        if constexpr (kWT) {
+            wt.refresh();
+            if constexpr (!EXACT)
+                asm volatile("" : "+s"(nl));
+        }
+        const uint32_t c = (uint32_t)(t % nl);
         const uint64_t i = t * tile + threadIdx.x;
         if (i >= p.nvec)
             continue;
         u32x4 v[RMAX];
 #pragma unroll
         for (int j = 0; j < RMAX; ++j)
-            if (EXACT || j < (int)n)
-                v[j] = load16<NT>((const u32x4 *)p.rk.send[j] + i);
+            if (EXACT || j < (int)nl)
+                v[j] = load16<NT>((const u32x4 *)(kWT ? wt.send(j) : p.rk.send[j]) + i);
         u32x4 y;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -59,7 +75,7 @@ __global__ __launch_bounds__(staged_max_threads(RMAX)) void hb_stage_reduce(Stag
             T::widen(v[0][q], acc);
 #pragma unroll
             for (int j = 1; j < RMAX; ++j) {
-                if (EXACT || j < (int)n) {
+                if (EXACT || j < (int)nl) {
                     float x[T::kPerWord];
                     T::widen(v[j][q], x);
 #pragma unroll
@@ -69,7 +85,7 @@ __global__ __launch_bounds__(staged_max_threads(RMAX)) void hb_stage_reduce(Stag
             }
             y[q] = T::narrow(acc);
         }
-        store16<NT>((u32x4 *)p.rk.recv[c] + i, y);
+        store16<NT>((u32x4 *)(kWT ? wt.recv(c) : p.rk.recv[c]) + i, y);
     }
 
     // Elements after the last whole vector: too few to stage; the last
@@ -103,16 +119,26 @@ __global__ __launch_bounds__(staged_max_threads(RMAX)) void hb_stage_gather(Stag
     const uint32_t n = EXACT ? RMAX : p.nranks;
     const uint64_t tile = blockDim.x;
     const uint64_t ntiles = (p.nvec + tile - 1) / tile;
+    constexpr bool kWT = staged_wave_table(RMAX, EXACT);
+    WaveTable<RMAX> wt;
+    if constexpr (kWT)
+        wt = WaveTable<RMAX>(p.rk);
     for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const uint32_t c = (uint32_t)(t % n);
+        uint32_t nl = n;
+        if constexpr (kWT) {
+            wt.refresh();
+            if constexpr (!EXACT)
+                asm volatile("" : "+s"(nl));
+        }
+        const uint32_t c = (uint32_t)(t % nl);
         const uint64_t i = t * tile + threadIdx.x;
         if (i >= p.nvec)
             continue;
-        const u32x4 y = load16<NT>((const u32x4 *)p.rk.recv[c] + i);
+        const u32x4 y = load16<NT>((const u32x4 *)(kWT ? wt.recv(c) : p.rk.recv[c]) + i);
 #pragma unroll
         for (int r = 0; r < RMAX; ++r)
-            if ((EXACT || r < (int)n) && r != (int)c)
-                store16<NT>((u32x4 *)p.rk.recv[r] + i, y);
+            if ((EXACT || r < (int)nl) && r != (int)c)
+                store16<NT>((u32x4 *)(kWT ? wt.recv(r) : p.rk.recv[r]) + i, y);
     }
 }
 

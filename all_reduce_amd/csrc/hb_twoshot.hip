@@ -223,8 +223,9 @@ __global__ __launch_bounds__(hb_max_threads(RMAX)) void hb_twoshot(HBParams<RMAX
 // 64 pointers do not fit: the compiler spills them and reloads them in blocks.
 // Same chunks, same order of additions, same results.  On MI355X, bf16 and
 // fp16: 3.6 against 4.8 us at 2 KiB per rank, 6.1 against 7.1 us at 512 KiB,
-// 189 against 191 us at 16 MiB (24 ranks: 4.6 against 6.4 us at 2 KiB); at
-// 112 MiB per rank of fp32 the scalar table is 1-2 % faster, so the launch
+// 188-189 against 192-194 us at 16 MiB (24 ranks on the generic table, with
+// its -0 slots: 4.1 against 6.4 us at 2 KiB); at 112 MiB per rank of fp32
+// the scalar table is 1-2 % faster, so the launch
 // takes this kernel up to kWaveTableMaxBytes per rank.  A separate kernel
 // rather than a switch in the one above, whose code stays as it is.
 template <typename T, bool EXACT, bool NT, int NODE>
@@ -354,7 +355,7 @@ template <typename T, int RMAX, bool EXACT, int U, bool NT, int NODE = 0>
 hipError_t launch_one(const HBParams<RMAX> &p, uint32_t grid, uint32_t threads, hipStream_t stream)
 {
     if constexpr (RMAX == 32 && U == 1) {
-        if (p.nvec * 16 <= kWaveTableMaxBytes) {
+        if (p.nvec * 16 <= kWaveTableMaxBytes && threads % 64 == 0) {
             hipLaunchKernelGGL((hb_twoshot_wave<T, EXACT, NT, NODE>), dim3(grid), dim3(threads), 0,
                                stream, p);
             return hipGetLastError();
