@@ -701,7 +701,6 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype_arg, int nranks,
     static const int kLLThreads[] = {128, 256, 512, 1024};
     static const int kLLBlocks[] = {1, 2, 4, 8, 16, 32, 64};
     static const int kHBThreads[] = {128, 256, 512};
-    const int hb_blocks[] = {comm->cu_count / 2, comm->cu_count, comm->cu_count * 2};
 
     const int top = bucket_of(maxBytesPerRank);
     for (int b = 9; b <= top && result == arSuccess; ++b) {
@@ -714,6 +713,10 @@ arResult_t arCommTune(arComm_t comm, arDataType_t dtype_arg, int nranks,
         const double est_us = (double)(2 * (size_t)nranks * bytes) / 5.0e6 + 3.0;
         int calls = (int)(200.0 / est_us);
         calls = calls < 5 ? 5 : (calls > 20 ? 20 : calls);
+        // HB workgroups: half, once and twice the default count for this size
+        // (one per CU, or more per CU for few ranks and large messages)
+        const int hb_default = comm->cu_count * ar::hb_default_blocks_per_cu(nranks, (uint64_t)bytes);
+        const int hb_blocks[] = {hb_default / 2, hb_default, hb_default * 2};
         for (int m = 0; m < 4 && result == arSuccess; ++m) {
             const int proto = m / 2 == 0 ? arProtoLL : arProtoHB;
             const int in_place = m % 2;  // in place: the send plane is also the receive plane

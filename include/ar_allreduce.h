@@ -294,7 +294,8 @@ arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
  * maxBytesPerRank per rank (the last bucket at maxBytesPerRank itself) is
  * timed with each protocol the communicator can run at that size, in place
  * and out of place (the two favour different shapes), over the built-in
- * default shape and a fixed set of candidates; a candidate wins only if it is
+ * default shape and a grid of candidates around it (HB: half, once and twice
+ * the default workgroup count); a candidate wins only if it is
  * more than 3 % faster than the best before it, and the winner and its time
  * are stored in the communicator.  Later calls of that dtype and rank count
  * use the stored shape of their size bucket (the message size rounded up to a
