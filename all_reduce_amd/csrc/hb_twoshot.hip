@@ -461,6 +461,16 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     uint64_t bpc = tiles < want ? tiles : want;
     if (bpc < 1)
         bpc = 1;
+    // A few more workgroups than that when they save a round of tiles while
+    // each workgroup has few (12 ranks at 512 KiB per rank: 22 tiles per
+    // chunk on 21 workgroups gave one of them a second tile); with many
+    // rounds one more costs less than the uneven load of the extra groups.
+    const uint64_t rounds = (tiles + bpc - 1) / bpc;
+    if (want_blocks == 0 && rounds > 1 && rounds <= 4) {
+        const uint64_t fewer = (tiles + rounds - 2) / (rounds - 1);
+        if (fewer * (uint64_t)nranks * 4 <= blocks * 5)
+            bpc = fewer;
+    }
     p.blocks_per_chunk = (uint32_t)bpc;
     const uint32_t grid = (uint32_t)(bpc * (uint64_t)nranks);
     if (cfg.rec != nullptr)
