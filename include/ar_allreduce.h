@@ -95,7 +95,8 @@ typedef enum {
      * one per compute unit, more from 4 MiB per rank for fewer than 6 ranks
      * (8 per CU at 1 rank down to 2 at 4 and 5) and for 9 to 15 ranks (2, or 4
      * above 16 MiB), where one per CU keeps too few loads in flight (measured
-     * on MI355X). */
+     * on MI355X); the default takes up to a quarter more workgroups where
+     * that saves a workgroup a round of tiles (at most four rounds). */
     arOptHBBlocks = 2,
     /* HB: 1 = non-temporal loads and stores, 0 = ordinary (cached) ones.
      * -1 (default): the policy the tuner chose for the message size and mode,
