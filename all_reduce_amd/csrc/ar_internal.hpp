@@ -73,11 +73,16 @@ inline LLShape ll_dense_default_shape(int nranks, uint64_t bytes_per_rank)
 // Bytes per rank from which three-element packets are the default: measured
 // on MI355X, they cost about 0.5 us of LDS staging per call at small sizes and
 // win from 256 KiB per rank at 8 ranks (1 MiB: 7.95 against 9.79 us; 192 KiB
-// still goes to word packets, 4.05 against 4.23 us), above 128 KiB at 9 to 16
-// ranks (128 KiB: word 4.6 against 4.9 us at 16 ranks; 136 KiB: 5.2 against
-// 6.3 us) and from 128 KiB above 16 (1 MiB at 32: 28.5 against 37.7 us).
+// still goes to word packets, 4.05 against 4.23 us) and at the generic counts
+// 3, 5, 6 and 7, above 512 KiB at 1, 2 and 4 ranks (2 ranks: word 4.8 against
+// 6.6 us at 512 KiB, three-element 5.4 against 5.6 us at 640 KiB), above
+// 128 KiB at 9 to 16 ranks (128 KiB: word 4.6 against 4.9 us at 16 ranks;
+// 136 KiB: 5.2 against 6.3 us) and from 128 KiB above 16 (1 MiB at 32: 28.5
+// against 37.7 us).
 inline uint64_t ll_dense_from_bytes(int nranks)
 {
+    if (nranks == 1 || nranks == 2 || nranks == 4)
+        return ((uint64_t)512 << 10) + 1;
     if (nranks <= 8)
         return (uint64_t)256 << 10;
     return nranks <= 16 ? ((uint64_t)128 << 10) + 1 : ((uint64_t)128 << 10);

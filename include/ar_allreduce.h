@@ -203,8 +203,8 @@ typedef enum {
      * third fewer packet and clear bytes than the word packet, whose
      * 4-byte payload sits next to a 4-byte flag.  0: the word packet.
      * -1 (default): three-element packets from the size where they measured
-     * faster on MI355X (256 KiB per rank up to 8 ranks, above 128 KiB from 9
-     * to 16, 128 KiB above 16),
+     * faster on MI355X (above 512 KiB per rank at 1, 2 and 4 ranks, 256 KiB
+     * at 3 and 5 to 8, above 128 KiB from 9 to 16, 128 KiB above 16),
      * word packets below, where their LDS staging costs more than the bytes
      * they save.
      * Applies to the flat order, the cleared flag scheme and 8-byte packets;

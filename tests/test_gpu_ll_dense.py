@@ -82,10 +82,14 @@ def test_in_place(comm, orc, dtype, R, N):
 
 
 def test_default_picks_the_format_by_size(comm, orc):
-    """By default bfloat16 / float16 take three-element packets from 256 KiB
-    per rank up to 8 ranks, above 128 KiB from 9 to 16 ranks and from 128 KiB
-    above 16, word packets below; float32 always word packets."""
+    """By default bfloat16 / float16 take three-element packets above 512 KiB
+    per rank at 1, 2 and 4 ranks, from 256 KiB at 3 and 5 to 8 ranks, above
+    128 KiB from 9 to 16 ranks and from 128 KiB above 16, word packets below;
+    float32 always word packets."""
     for R, n, dtype, payload in ((8, (256 << 10) // 2, "bf16", 6), (8, (192 << 10) // 2, "bf16", 4),
+                                 (2, (512 << 10) // 2, "bf16", 4), (2, (640 << 10) // 2, "bf16", 6),
+                                 (4, (512 << 10) // 2, "fp16", 4), (4, (1 << 20) // 2, "fp16", 6),
+                                 (3, (256 << 10) // 2, "bf16", 6), (6, (256 << 10) // 2, "bf16", 6),
                                  (16, (256 << 10) // 2, "fp16", 6), (16, (128 << 10) // 2, "fp16", 4),
                                  (16, (128 << 10) // 2 + 1, "fp16", 6), (12, (136 << 10) // 2, "bf16", 6),
                                  (12, (128 << 10) // 2, "bf16", 4),
