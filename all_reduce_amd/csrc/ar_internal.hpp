@@ -18,13 +18,16 @@ constexpr int kRankVariants = 6;  // 1, 2, 4, 8, 16, 32 -> exact kernels; others
 constexpr int kThreadChoices = 5; // 64, 128, 256, 512, 1024
 
 // Default LL launch shape for a call that names none and has no tuned entry:
-// threads per workgroup and workgroups per rank, by rank count (up to 8,
+// threads per workgroup and workgroups per rank, by rank count (up to 4, 5-8,
 // 9-16, 17-32) and message size per rank, for 8-byte packets.  Each entry is
 // the fastest of a grid measured on MI355X (bf16, graph-replayed calls,
 // 64-1024 threads, 1-128 workgroups per rank) at a power-of-two size from
 // 2 KiB to 1 MiB per rank, or one within measurement noise of it that is also
 // the best at a neighbouring size.  A size takes the entry of the next power
-// of two up, and sizes above 1 MiB the last one.
+// of two up, and sizes above 1 MiB the last one.  The first two rows differ
+// at 256 and 512 KiB, where up to 4 ranks word packets run with 512 x 64
+// (bf16 at 2 ranks, 512 KiB: 3.85 against 4.86 us with 512 x 32; 4 ranks
+// 4.33 against 4.91) and at 8 ranks (fp32) 256 x 32 and 512 x 32 lead.
 struct LLShape {
     int threads;
     int per_rank;
@@ -32,9 +35,11 @@ struct LLShape {
 
 inline LLShape ll_default_shape(int nranks, uint64_t bytes_per_rank)
 {
-    static constexpr LLShape kTable[3][10] = {
+    static constexpr LLShape kTable[4][10] = {
         // 2K        4K        8K        16K       32K        64K
         // 128K      256K       512K       1M
+        {{256, 1}, {256, 2}, {256, 4}, {256, 8}, {256, 16}, {256, 64},
+         {256, 64}, {512, 64}, {512, 64}, {512, 32}},
         {{256, 1}, {256, 2}, {256, 4}, {256, 8}, {256, 16}, {256, 64},
          {256, 64}, {256, 32}, {512, 32}, {512, 32}},
         {{512, 1}, {512, 1}, {512, 2}, {512, 4}, {256, 8}, {256, 32},
@@ -45,7 +50,7 @@ inline LLShape ll_default_shape(int nranks, uint64_t bytes_per_rank)
     int s = 0;
     while (s < 9 && ((uint64_t)2048 << s) < bytes_per_rank)
         ++s;
-    return kTable[nranks <= 8 ? 0 : (nranks <= 16 ? 1 : 2)][s];
+    return kTable[nranks <= 4 ? 0 : (nranks <= 8 ? 1 : (nranks <= 16 ? 2 : 3))][s];
 }
 
 // The same for the three-element packets of bfloat16 and float16 (ll_dense.hip),

@@ -465,8 +465,15 @@ hipError_t launch_table(const void *const *send, void *const *recv, size_t count
     // each workgroup has few (12 ranks at 512 KiB per rank: 22 tiles per
     // chunk on 21 workgroups gave one of them a second tile); with many
     // rounds one more costs less than the uneven load of the extra groups.
+    // At one workgroup per CU, two rounds become one with up to twice the
+    // workgroups (16 ranks at 1 MiB per rank: 512 workgroups, 5.5 against
+    // 6.6 us; 32 ranks 10.4 against 11.5 us); with more rounds, or more
+    // workgroups per CU already, the extra groups weigh more.
     const uint64_t rounds = (tiles + bpc - 1) / bpc;
-    if (want_blocks == 0 && rounds > 1 && rounds <= 4) {
+    if (want_blocks == 0 && rounds == 2 && tiles <= 2 * bpc &&
+        blocks <= (uint64_t)cfg.cu_count) {
+        bpc = tiles;
+    } else if (want_blocks == 0 && rounds > 1 && rounds <= 4) {
         const uint64_t fewer = (tiles + rounds - 2) / (rounds - 1);
         if (fewer * (uint64_t)nranks * 4 <= blocks * 5)
             bpc = fewer;
