@@ -298,8 +298,10 @@ arResult_t arCommGetOption(arComm_t comm, arOption_t option, int64_t *value);
  * and out of place (the two favour different shapes), over the built-in
  * default shape and a grid of candidates around it (HB: half, once and twice
  * the default workgroup count); a candidate wins only if it is
- * more than 3 % faster than the best before it, and the winner and its time
- * are stored in the communicator.  Later calls of that dtype and rank count
+ * more than 3 % faster than the best before it, a winner other than the
+ * default shape and access policy is timed again beside the default and kept
+ * only if it is still more than 3 % faster (else the default is stored), and
+ * the stored shape and its time are kept in the communicator.  Later calls of that dtype and rank count
  * use the stored shape of their size bucket (the message size rounded up to a
  * power of two) and mode (in place: recvbufs[r] == sendbufs[r] for every
  * rank) unless arOptLLThreads/arOptLLBlocksPerRank (LL) or arOptHBThreads/
