@@ -217,7 +217,10 @@ __global__ __launch_bounds__(kDenseMaxThreads) void ll_dense(LLDenseParams<RMAX>
                 }
             }
         }
-        // reduce in rank order, clear what was read, stage the results
+        // reduce in rank order, then clear what was read, then stage the
+        // results.  Every index's sum is taken before the first clear: gfx9
+        // counts loads and stores on one counter, so a packet value used after
+        // a store would make the wave wait for that store's completion too.
         uint32_t y01[GB], y2[GB];
 #pragma unroll
         for (int v = 0; v < GB; ++v) {
@@ -242,11 +245,16 @@ __global__ __launch_bounds__(kDenseMaxThreads) void ll_dense(LLDenseParams<RMAX>
                 a[3] = 0.0f;
                 y01[v] = T::narrow(a);
                 y2[v] = T::narrow(a + 2) & 0xffffu;
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < GB; ++v) {
+            const uint64_t q = qb + lane + 64u * v;
+            if (q < g1 && !gave_up)
 #pragma unroll
                 for (int j = 0; j < RMAX; ++j)
                     if (EXACT || j < (int)nl)
                         put_packet(p.pkts + (uint64_t)j * p.pkt_stride + q, 0u, 0u);
-            }
         }
         wave_lds_sync();  // the previous round's output reads are done
         // index rel's three results go to bytes [6 rel, 6 rel + 6), in
