@@ -659,7 +659,9 @@ def run_c5(B, inputs, fp16=True):
     chunk = N/R (the configured layout) beside the interleaved default:
     C5a 2^18 fp16 per rank, graph-replayed (plus LL at the same size; the
     runs' timing passes taken in turn), and C5b 4096 x 7168 fp32 per rank
-    (112 MiB), back-to-back launches, out of place.  Each row checks the
+    (112 MiB), back-to-back launches, out of place, with the cold per-call
+    mean and median beside them (last-level cache flushed before each call).
+    Each row checks the
     oracle (C5b on 2^20 sampled columns), that all R outputs are equal, and
     that rank 0's equals the exact integer sum."""
     torch = B.torch
@@ -720,21 +722,29 @@ def run_c5(B, inputs, fp16=True):
                 times = timed[lname, proto]
                 us, med, mode = statistics.median(times), times[0], "graph, median"
             else:
+                # back to back, and per call with the last-level cache flushed
+                # before each one (the prefill's cold protocol; out of place,
+                # so nothing is restored)
                 B.comm.set_option(O.arOptHBChunkLayout, layout)
                 try:
                     for _ in range(B.args.warmup):
                         B.launch(sv, rv, n, proto)
                     us = B.back_to_back_us(sv, rv, n, proto, B.args.steps)
+                    cold = B.cold_us(None, None, sv, rv, n, proto, B.args.steps, B.args.warmup)
                 finally:
                     B.comm.set_option(O.arOptHBChunkLayout, 1)
                 med, mode = None, "back-to-back"
             g = gbps(R, n, es, us)
-            rows.append({"config": name, "R": R, "dtype": dtype, "elems_per_rank": n,
-                         "bytes_per_rank": n * es, "proto": proto, "chunk_layout": lname,
-                         "mode": mode, "us": round(us, 3),
-                         "us_first_pass": None if med is None else round(med, 3), "gbps": g,
-                         "pct_of_peak": round(100 * g / HBM_PEAK_GBPS, 2), "parity": par,
-                         "exact_integer_sums": ex, "launch": rec})
+            row = {"config": name, "R": R, "dtype": dtype, "elems_per_rank": n,
+                   "bytes_per_rank": n * es, "proto": proto, "chunk_layout": lname,
+                   "mode": mode, "us": round(us, 3),
+                   "us_first_pass": None if med is None else round(med, 3), "gbps": g,
+                   "pct_of_peak": round(100 * g / HBM_PEAK_GBPS, 2), "parity": par,
+                   "exact_integer_sums": ex, "launch": rec}
+            if name == "C5b":
+                row["us_cold_mean"] = round(statistics.fmean(cold), 2)
+                row["us_cold_median"] = round(statistics.median(cold), 2)
+            rows.append(row)
             log(f"{name} R={R} {dtype} {proto} ({lname}): {us:.2f} us, {g:.0f} GB/s "
                 f"({100 * g / HBM_PEAK_GBPS:.1f}% of 8 TB/s), parity {par}, exact {ex}")
         del x, sv, rv, exact

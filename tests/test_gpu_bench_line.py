@@ -97,3 +97,9 @@ def test_c5_rows():
     for r in rows:
         assert r["gbps"] == pytest.approx(
             2 * r["R"] * r["bytes_per_rank"] / (r["us"] * 1e-6) / 1e9, rel=2e-3)
+    # C5b is also timed per call with the last-level cache flushed first
+    for r in rows:
+        if r["config"] == "C5b":
+            assert 0 < r["us_cold_median"] and 0 < r["us_cold_mean"]
+        else:
+            assert "us_cold_mean" not in r
