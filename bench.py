@@ -190,11 +190,14 @@ class Bench:
         return round(statistics.median(ts) * 1e3, 3)
 
     # -- timings ------------------------------------------------------------
-    def graph_passes(self, sv, rv, n, proto, passes=1, call=None):
+    def graph_passes(self, sv, rv, n, proto, passes=1, call=None, check=None):
         """µs per call: 10 calls per graph, warmup replays, then ``passes``
         timed passes of steps replays, each inside its own event pair.
         ``call`` (optional) makes one call on the current stream instead of
-        arAllReduce with the communicator."""
+        arAllReduce with the communicator.  With ``check`` (out of place
+        only), the outputs are zeroed after capture, the graph is replayed
+        once, and ``check()`` (the oracle comparison) is kept in
+        ``last_graph_parity`` before the warm-up replays."""
         torch = self.torch
         one = call if call is not None else (lambda: self.launch(sv, rv, n, proto))
         side = torch.cuda.Stream()
@@ -208,6 +211,13 @@ class Bench:
         with torch.cuda.graph(g):
             for _ in range(CALLS_PER_GRAPH):
                 one()
+        self.last_graph_parity = None
+        if check is not None:
+            for t in rv:
+                t.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            self.last_graph_parity = check()
         for _ in range(self.args.warmup):
             g.replay()
         torch.cuda.synchronize()
@@ -362,8 +372,11 @@ def main():
                 row[f"{proto}_launch"] = B.launch_record(proto)
                 row[f"{proto}_parity"] = B.parity(x, rv)
                 # the first pass is the guide's protocol (--steps replays in one
-                # event pair); four more give the median beside it
-                times = B.graph_passes(sv, rv, n, proto, passes=MEDIAN_PASSES)
+                # event pair); four more give the median beside it.  The graph's
+                # own first replay is checked against the oracle too.
+                times = B.graph_passes(sv, rv, n, proto, passes=MEDIAN_PASSES,
+                                       check=lambda: B.parity(x, rv))
+                row[f"{proto}_parity_graph"] = B.last_graph_parity
                 row[f"{proto}_us"] = round(times[0], 3)
                 row[f"{proto}_us_median"] = round(statistics.median(times), 3)
                 row[f"{proto}_gbps"] = gbps(R, n, 2, times[0])
@@ -388,7 +401,9 @@ def main():
             torch.cuda.synchronize()
             dec[f"{proto}_launch"] = B.launch_record(proto)
             dec[f"{proto}_parity"] = B.parity(x, rv)
-            times = B.graph_passes(sv, rv, n, proto, passes=MEDIAN_PASSES)
+            times = B.graph_passes(sv, rv, n, proto, passes=MEDIAN_PASSES,
+                                   check=lambda: B.parity(x, rv))
+            dec[f"{proto}_parity_graph"] = B.last_graph_parity
             dec[f"{proto}_us"] = round(times[0], 3)
             dec[f"{proto}_us_median"] = round(statistics.median(times), 3)
         result["decode_64x8192"] = dec

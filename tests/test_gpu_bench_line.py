@@ -47,6 +47,10 @@ def test_sweep_line():
     rows = line["ll_sweep"]
     assert [r["bytes_per_rank"] for r in rows] == [2 << k for k in range(10, 20)]
     assert all(r["ll_parity"] and r["hb_parity"] for r in rows)
+    # the graph's own first replay (outputs zeroed after capture) is exact too
+    assert all(r["ll_parity_graph"] and r["hb_parity_graph"] for r in rows)
+    dec = line["decode_64x8192"]
+    assert dec["ll_parity_graph"] and dec["hb_parity_graph"]
     assert line["value"] == pytest.approx(sum(r["ll_us"] for r in rows) / len(rows), abs=2e-3)
     # the floor is a one-workgroup call: below the slowest LL call on any machine
     assert 0 < line["graph_floor_us"] < max(r["ll_us"] for r in rows)
